@@ -1,0 +1,69 @@
+// Internal interface between the host layer (host.cpp) and the kernel files.
+// Everything here has been validated by the host layer before a launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sparstar {
+
+// Geometry of one scale, already derived on the host.
+struct Geometry {
+  int32_t B, H, D, b;
+  int64_t L_q, L_k;
+  int32_t n_q, n_k;
+};
+
+struct PoolScoreArgs {
+  Geometry g;
+  int dtype;                 // 0 bf16, 1 f32
+  const void* q;
+  const void* k;
+  int64_t qs_b, qs_h, qs_t;  // element strides
+  int64_t ks_b, ks_h, ks_t;
+  float* q_pool;             // [B,H,n_q,D]
+  float* k_pool;             // [B,H,n_k,D]
+  float* scores;             // [B,H,n_q,n_k]
+  float sigma;
+};
+
+struct SelectArgs {
+  const float* scores;       // [rows, n_k]
+  int32_t n_k;
+  int32_t n_keep;            // retained prefix [0, n_keep)
+  int32_t k;                 // candidates taken per row
+  int64_t rows;              // B*H*n_q
+  int32_t* row_ptr;          // [rows + 1]
+  int32_t* col_idx;
+};
+
+struct AttnArgs {
+  Geometry g;
+  int dtype;                 // q/k/v dtype
+  int out_dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;                // nullable, [B,H,L_q]
+  int64_t qs_b, qs_h, qs_t;
+  int64_t ks_b, ks_h, ks_t;
+  int64_t vs_b, vs_h, vs_t;
+  int64_t os_b, os_h, os_t;
+  const int32_t* row_ptr;    // nullptr => dense (every key block)
+  const int32_t* col_idx;
+  int64_t col_idx_len;
+  float sigma;
+};
+
+hipError_t launch_pool_score(const PoolScoreArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// bf16 inputs, D = 128, b = 128 (MFMA path).
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+// Any supported shape/dtype (float32 path).
+hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t s);
+
+// Largest candidate count one select wavefront holds in registers.
+constexpr int kSelectMaxCandidates = 64 * 64;
+
+}  // namespace sparstar

@@ -172,25 +172,40 @@ def _round(x: np.ndarray, dtype: str):
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
-def make_inputs(cfg: ScaleConfig, device: str = "cpu", heads: Optional[Iterable[int]] = None):
+def make_inputs(cfg: ScaleConfig, device: str = "cpu", heads: Optional[Iterable[int]] = None,
+                workers: int = 0):
     """Q [B,H,L_q,D], K, V [B,H,L_k,D] as torch tensors in the workload dtype.
 
-    Tensors are filled head by head, so peak host memory stays near one
-    head's float32 draws even at the 720p sizes.  ``heads`` restricts the
+    Heads are drawn independently (each from its own seed), ``workers``
+    threads at a time (0: up to 16, bounded by the CPU count), and copied
+    into the tensors as they finish, so host memory stays near ``workers``
+    heads of float32 draws even at the 720p sizes.  ``heads`` restricts the
     draw to a subset (the other heads are left uninitialised).
     """
+    import concurrent.futures as cf
+
     import torch
     tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     B, H, D = cfg.batch, cfg.heads, cfg.head_dim
     Q = torch.empty((B, H, cfg.len_q, D), dtype=tdtype, device=device)
     K = torch.empty((B, H, cfg.len_k, D), dtype=tdtype, device=device)
     V = torch.empty((B, H, cfg.len_k, D), dtype=tdtype, device=device)
-    for b in range(B):
-        for h in (range(H) if heads is None else heads):
-            hi = draw_head(cfg, h, b)
-            Q[b, h].copy_(_round(hi.q, cfg.dtype))
-            K[b, h].copy_(_round(hi.k, cfg.dtype))
-            V[b, h].copy_(_round(hi.v, cfg.dtype))
+    jobs = [(b, h) for b in range(B) for h in (range(H) if heads is None else heads)]
+    if workers <= 0:
+        import os
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), len(jobs)))
+
+    def draw(job):
+        b, h = job
+        hi = draw_head(cfg, h, b)
+        return job, [_round(x, cfg.dtype) for x in (hi.q, hi.k, hi.v)]
+
+    with cf.ThreadPoolExecutor(workers) as ex:
+        for i in range(0, len(jobs), workers):
+            for (b, h), (q, k, v) in ex.map(draw, jobs[i:i + workers]):
+                Q[b, h].copy_(q)
+                K[b, h].copy_(k)
+                V[b, h].copy_(v)
     return Q, K, V
 
 

@@ -1,0 +1,172 @@
+/*
+ * sparstar.h -- C ABI of libsparstar: SparSTAR dynamic block-sparse attention
+ * for one expensive scale of spacetime-autoregressive video generation, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video
+ * Synthesis" (full text), section 5 "Method".  For every (batch, head):
+ *   1. mean-pool contiguous query and key blocks of b tokens        (sparstar_pool_score)
+ *   2. score every (query block, key block) pair, S = sigma*Qbar*Kbar^T (sparstar_pool_score)
+ *   3. keep the designated context blocks, rank the rest per query
+ *      block and keep the top fraction rho, as a CSR block list     (sparstar_select_blocks)
+ *   4. attend each query block to its listed key blocks only       (sparstar_bsa_fwd)
+ * and a dense forward over every key block as the density-1 baseline
+ * (dense_attn_fwd).
+ *
+ * Layout.  Q is [B, H, L_q, D]; K and V are [B, H, L_k, D] with the key
+ * sequence ordered [text | reference | current], L_k = L_text + L_ref + L_q:
+ * the current-scale tokens are both the queries and the last L_q keys
+ * (section 3 "Spacetime Sparse Attention").  Strides are in elements for the
+ * batch, head and token dimensions; the head_dim stride is 1.
+ *
+ * Blocks.  Query block i holds tokens [i*b, min((i+1)*b, L_q)); key block j
+ * holds [j*b, min((j+1)*b, L_k)); n_q = ceil(L_q/b), n_k = ceil(L_k/b).
+ * Blocks are not aligned to the text/reference/current boundaries (section 5
+ * "Original-order block partition").
+ *
+ * Memory and streams.  Every pointer passed to a device call is a device
+ * pointer owned by the caller.  The library never allocates or frees device
+ * memory, never synchronises, and keeps no pointer after a call returns.  Each
+ * device call validates all of its arguments on the host first; a non-OK
+ * status means nothing was enqueued.  After validation, work is enqueued on
+ * `stream` (a hipStream_t; NULL is the default stream) and the call returns
+ * without waiting.  A fault inside a kernel surfaces at the caller's next
+ * synchronisation.  Outputs must not alias inputs.  Calls are reentrant; the
+ * last-error text is per thread.
+ */
+#ifndef SPARSTAR_H
+#define SPARSTAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARSTAR_OK = 0,
+  SPARSTAR_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  SPARSTAR_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree                */
+  SPARSTAR_ERR_UNSUPPORTED = 3, /* valid but not built: head_dim, block, dtype, device     */
+  SPARSTAR_ERR_LAYOUT = 4,      /* stride or pointer alignment not supported               */
+  SPARSTAR_ERR_DENSITY = 5,     /* density not in (0, 1]                                  */
+  SPARSTAR_ERR_CAPACITY = 6,    /* an output buffer is smaller than the result             */
+  SPARSTAR_ERR_HIP = 7          /* the HIP runtime reported an error                       */
+} sparstar_status;
+
+typedef enum { SPARSTAR_BF16 = 0, SPARSTAR_F32 = 1 } sparstar_dtype;
+
+/* Which key blocks stay dense and which are ranked (section 5 "Clip-Dependent
+ * Retained and Selectable Blocks"; appendix A.7 "Later-clip schedule").
+ * LATER_CLIP (clip c >= 2): the blocks touching the text stay; reference and
+ *   current blocks are ranked jointly under one budget.
+ * FIRST_CLIP (clip 1): the blocks touching the text or the reference (for clip
+ *   1 the final image-pyramid scale) stay; only the rest are ranked.
+ * In both the retained set is the prefix of key blocks [0, r) and the ranked
+ * candidates are [r, n_k). */
+typedef enum { SPARSTAR_POLICY_LATER_CLIP = 0, SPARSTAR_POLICY_FIRST_CLIP = 1 } sparstar_policy;
+
+typedef struct {
+  int32_t batch;          /* B >= 0                                                     */
+  int32_t heads;          /* H >= 0                                                     */
+  int32_t head_dim;       /* D: 64 or 128                                               */
+  int32_t block;          /* b: 64 or 128, the same for query and key blocks            */
+  int64_t len_q;          /* L_q >= 0: current-scale tokens (queries, last keys)        */
+  int64_t len_text;       /* L_text >= 0                                                */
+  int64_t len_ref;        /* L_ref >= 0: the preceding clip's final scale               */
+  int32_t dtype;          /* sparstar_dtype of Q, K, V                                  */
+  int32_t out_dtype;      /* sparstar_dtype of the attention output                     */
+  float softmax_scale;    /* sigma > 0, finite (1/sqrt(D) in the workloads)            */
+  int32_t reserved;       /* must be 0                                                  */
+  int64_t q_stride[3];    /* element strides of Q over (batch, head, token)            */
+  int64_t k_stride[3];    /* ... of K                                                   */
+  int64_t v_stride[3];    /* ... of V                                                   */
+  int64_t o_stride[3];    /* ... of the output                                          */
+} sparstar_problem;
+
+/* ---------------- host-only helpers: no HIP call, usable without a GPU ---------------- */
+
+/* Validates the problem description alone (sizes, dtypes, strides, scale). */
+sparstar_status sparstar_check_problem(const sparstar_problem* p);
+
+/* n_q = ceil(L_q/b) and n_k = ceil(L_k/b); -1 if the problem is invalid. */
+int64_t sparstar_num_q_blocks(const sparstar_problem* p);
+int64_t sparstar_num_k_blocks(const sparstar_problem* p);
+
+/* Number r of retained key blocks under `policy` (the prefix [0, r)); -1 if invalid. */
+int64_t sparstar_num_retained(const sparstar_problem* p, int32_t policy);
+
+/* Budget k for n_candidates ranked blocks at `density` (section 5 "Clip-Dependent
+ * Retained and Selectable Blocks"): k = ceil(density*n - 1e-6) clamped to [1, n],
+ * and 0 if n == 0; -1 if density is not in (0, 1] or n < 0. */
+int64_t sparstar_budget(int64_t n_candidates, double density);
+
+/* Key blocks listed per query block: r + k; -1 if invalid. */
+int64_t sparstar_blocks_per_row(const sparstar_problem* p, double density, int32_t policy);
+
+/* Entries of col_idx written by sparstar_select_blocks: B*H*n_q*(r + k); -1 if invalid. */
+int64_t sparstar_select_nnz(const sparstar_problem* p, double density, int32_t policy);
+
+const char* sparstar_status_string(sparstar_status s);
+
+/* Detail text of the last non-OK status returned on this thread ("" if none). */
+const char* sparstar_last_error(void);
+
+/* ---------------- device calls: pointers are device pointers; async on `stream` ------- */
+
+/* Steps 1-2 (section 5 "Original-order block partition", "Per-head aggregated
+ * query-key score").
+ *   q, k     : inputs in p->dtype with p's strides.
+ *   q_pool   : out, float32 [B, H, n_q, D] contiguous: q_pool[i] = (1/b) * sum of the
+ *              real tokens of query block i (a partial last block is zero-padded
+ *              and still divided by b).
+ *   k_pool   : out, float32 [B, H, n_k, D] contiguous, likewise for key blocks.
+ *   scores   : out, float32 [B, H, n_q, n_k] contiguous: sigma * <q_pool_i, k_pool_j>.
+ * Sums and products are float32. */
+sparstar_status sparstar_pool_score(const sparstar_problem* p, const void* q, const void* k,
+                                    float* q_pool, float* k_pool, float* scores, void* stream);
+
+/* Step 3 (section 5 "Clip-Dependent Retained and Selectable Blocks" and
+ * "Forward-Only Sparse Execution"; appendix A.7).  For every row
+ * r = (b*H + h)*n_q + i the listed blocks are the retained prefix [0, r_keep)
+ * followed by the k best candidates of scores[b, h, i, r_keep:n_k], best meaning
+ * the larger score, exactly equal scores going to the lower block index; the
+ * list is ascending.  This is the forward-only BlockMask (kv_num_blocks,
+ * kv_indices) in CSR form.
+ *   scores   : in, float32 [B, H, n_q, n_k] contiguous (as written by pool_score).
+ *   row_ptr  : out, int32 [B*H*n_q + 1]; row_ptr[r] = r * (r_keep + k).
+ *   col_idx  : out, int32 [col_idx_capacity]; the first sparstar_select_nnz entries
+ *              are written.  SPARSTAR_ERR_CAPACITY if the capacity is smaller.
+ * NaN scores are not supported (their rank is unspecified). */
+sparstar_status sparstar_select_blocks(const sparstar_problem* p, const float* scores,
+                                       double density, int32_t policy, int32_t* row_ptr,
+                                       int32_t* col_idx, int64_t col_idx_capacity, void* stream);
+
+/* Step 4 (section 5 "Forward-Only Sparse Execution", "Complexity and Scope").
+ * Each query t of block i gets o_t = sum_s softmax_s(sigma * q_t.k_s) v_s over the
+ * real key tokens s (< L_k) of the blocks col_idx[row_ptr[r] .. row_ptr[r+1]),
+ * r = (b*H + h)*n_q + i.  Entries outside [0, n_k) and positions outside
+ * [0, col_idx_len) are skipped; a row with no valid block gets o = 0 and
+ * lse = -inf.  A block listed twice counts twice.
+ *   q, k, v  : inputs in p->dtype.
+ *   row_ptr  : in, int32 [B*H*n_q + 1];  col_idx: in, int32 [col_idx_len].
+ *   out      : out, p->out_dtype with p->o_stride; rows >= L_q are not written.
+ *   lse      : out, nullable, float32 [B, H, L_q] contiguous: sigma*max + log(sum exp).
+ * bf16 inputs with D = 128 and b = 128 run on bf16 MFMA with float32 softmax and
+ * accumulation; other shapes and float32 inputs run a float32 kernel. */
+sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const void* k,
+                                 const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                                 int64_t col_idx_len, void* out, float* lse, void* stream);
+
+/* Dense attention forward (every key block of every row): the density-1 baseline
+ * that the sparse operator is compared with (section 6 "End-to-end efficiency").
+ * Arguments as for sparstar_bsa_fwd without the block lists. */
+sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const void* k,
+                               const void* v, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSTAR_H */

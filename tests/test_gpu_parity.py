@@ -1,0 +1,369 @@
+"""GPU parity: every step of the HIP path against the float64 CPU oracle.
+
+All calls go through the C ABI (ctypes binding).  Inputs come from the
+seeded generator; the oracle reads the very values uploaded to the GPU."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_attention_aggregated_amd import inputs as I
+from block_sparse_attention_aggregated_amd import sparstar as S
+
+from parity import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, attention_errors, compare_row_selection,
+                    csr_rows, oracle_rows, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+_CACHE = {}
+
+
+def inputs(cfg):
+    key = cfg
+    if key not in _CACHE:
+        if len(_CACHE) >= 2:
+            _CACHE.clear()
+            torch.cuda.empty_cache()
+        _CACHE[key] = I.make_inputs(cfg, device=DEV)
+        torch.cuda.synchronize()
+    return _CACHE[key]
+
+
+def scale_of(cfg):
+    return S.Scale(cfg.len_text, cfg.len_ref, cfg.block, cfg.softmax_scale)
+
+
+def head_np(t, h):
+    return to_f64(t[0, h])
+
+
+def print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+# ---------------------------------------------------------------- pool + score
+
+@pytest.mark.parametrize("cfg,heads", [(I.TINY, None), (I.S192P, None), (I.S480P, [0, 23])])
+def test_pool_score_parity(cfg, heads):
+    print_case("pool_score", cfg.name)
+    Q, K, V = inputs(cfg)
+    qp, kp, sc = S.sparstar_pool_score(Q, K, scale_of(cfg))
+    torch.cuda.synchronize()
+    b, sigma = cfg.block, cfg.softmax_scale
+    for h in (range(cfg.heads) if heads is None else heads):
+        q, k = head_np(Q, h), head_np(K, h)
+        qbar, kbar = O.pool_blocks(q, b), O.pool_blocks(k, b)
+        S_ref = O.block_scores(qbar, kbar, sigma)
+        assert np.max(np.abs(to_f64(qp[0, h]) - qbar)) < 2e-6 * max(1.0, np.abs(qbar).max())
+        assert np.max(np.abs(to_f64(kp[0, h]) - kbar)) < 2e-6 * max(1.0, np.abs(kbar).max())
+        # float32 dot products of length D: error bounded by D * eps * sum |terms|
+        bound = cfg.head_dim * 6e-8 * sigma * (np.abs(qbar) @ np.abs(kbar).T) + 1e-7
+        err = np.abs(to_f64(sc[0, h]) - S_ref)
+        assert np.all(err <= bound), float((err / bound).max())
+
+
+# ---------------------------------------------------------------- selection
+
+@pytest.mark.parametrize("cfg,rho,policy", [(I.TINY, 0.5, 0), (I.TINY, 1.0, 0), (I.TINY, 0.25, 1),
+                                            (I.S192P, 0.3, 0), (I.S192P, 0.05, 1), (I.S192P, 1.0, 0)])
+def test_select_bitexact_on_oracle_scores(cfg, rho, policy):
+    """Given the same float32 scores, the GPU selection equals the oracle's exactly."""
+    print_case("select exact", cfg.name, rho, policy)
+    Q, K, V = inputs(cfg)
+    b, sigma = cfg.block, cfg.softmax_scale
+    S32 = torch.empty((1, cfg.heads, O.num_blocks(cfg.len_q, b), O.num_blocks(cfg.len_k, b)),
+                      dtype=torch.float32)
+    for h in range(cfg.heads):
+        S32[0, h] = torch.from_numpy(O.block_scores(O.pool_blocks(head_np(Q, h), b),
+                                                    O.pool_blocks(head_np(K, h), b), sigma))
+    # plant exact ties to exercise the lower-index rule
+    S32[0, 0, 0, -4:] = S32[0, 0, 0, -5]
+    rp, ci = S.sparstar_select_blocks(S32.to(DEV), Q, K, scale_of(cfg), rho, policy)
+    rows = csr_rows(rp, ci)
+    R, C = O.retained_and_candidates(cfg.len_text, cfg.len_ref, cfg.len_q, b, policy)
+    kk = O.budget(len(C), rho)
+    nq = O.num_blocks(cfg.len_q, b)
+    for h in range(cfg.heads):
+        ref = O.select_blocks(S32[0, h].double().numpy(), R, C, kk)
+        for i in range(nq):
+            assert np.array_equal(rows[h * nq + i], ref[i]), (h, i)
+
+
+@pytest.mark.parametrize("cfg,rho,heads", [(I.TINY, 0.5, None), (I.S192P, 0.3, None),
+                                           (I.S480P, 0.25, [0, 11, 23])])
+def test_select_parity_end_to_end(cfg, rho, heads):
+    """GPU scores -> GPU selection vs the oracle's own scores and selection (tie rule)."""
+    print_case("select e2e", cfg.name, rho)
+    Q, K, V = inputs(cfg)
+    sc = S.sparstar_pool_score(Q, K, scale_of(cfg))[2]
+    rp, ci = S.sparstar_select_blocks(sc, Q, K, scale_of(cfg), rho)
+    rows = csr_rows(rp, ci)
+    b = cfg.block
+    nq = O.num_blocks(cfg.len_q, b)
+    swaps = 0
+    for h in (range(cfg.heads) if heads is None else heads):
+        res = O.scale_head(head_np(Q, h), head_np(K, h), head_np(V, h), cfg.len_text, cfg.len_ref, b,
+                           cfg.softmax_scale, rho, rows=[])
+        for i in range(nq):
+            swaps += compare_row_selection(rows[h * nq + i], res["sets"][i], res["scores"][i],
+                                           len(res["retained"]), res["k"])
+    print(f"near-tie swaps: {swaps}")
+
+
+# ---------------------------------------------------------------- attention
+
+def _check_attention(cfg, Q, K, V, rows_lists, out, lse, heads, sample_rows, bf16_in):
+    b, sigma = cfg.block, cfg.softmax_scale
+    nq = O.num_blocks(cfg.len_q, b)
+    worst_max, sum_abs, n = 0.0, 0.0, 0
+    for h in heads:
+        q, k, v = head_np(Q, h), head_np(K, h), head_np(V, h)
+        lists = rows_lists[h * nq:(h + 1) * nq]
+        rows = range(nq) if sample_rows is None else sample_rows(h)
+        ref_o, ref_l = oracle_rows(q, k, v, lists, rows, b, sigma)
+        got = to_f64(out[0, h])
+        got_l = to_f64(lse[0, h]) if lse is not None else None
+        for i in rows:
+            s, e = O.block_range(i, cfg.len_q, b)
+            mx, mean = attention_errors(got[s:e], ref_o[i])
+            worst_max = max(worst_max, mx)
+            sum_abs += mean * (e - s) * cfg.head_dim
+            n += (e - s) * cfg.head_dim
+            if got_l is not None:
+                assert np.max(np.abs(got_l[s:e] - ref_l[i])) < (2e-3 if bf16_in else 1e-5), (h, i)
+    mean_abs = sum_abs / max(n, 1)
+    print(f"max-abs {worst_max:.3e} mean-abs {mean_abs:.3e} over {n // cfg.head_dim} queries")
+    if bf16_in:
+        assert worst_max <= BF16_MAX_ABS and mean_abs <= BF16_MEAN_ABS
+    else:
+        assert worst_max <= F32_MAX_ABS
+    return worst_max, mean_abs
+
+
+@pytest.mark.parametrize("cfg,rho,out_dtype,heads,nsample", [
+    (I.TINY, 0.5, torch.float32, None, None),
+    (I.TINY, 1.0, torch.float32, None, None),
+    (I.S192P, 0.3, torch.bfloat16, None, None),
+    (I.S192P, 0.3, torch.float32, [0, 7, 15], None),
+    (I.S480P, 0.25, torch.bfloat16, [0, 9, 23], 12),
+])
+def test_bsa_parity_on_gpu_csr(cfg, rho, out_dtype, heads, nsample):
+    """bsa_fwd against oracle attention over the GPU's own block lists."""
+    print_case("bsa", cfg.name, rho, out_dtype)
+    Q, K, V = inputs(cfg)
+    (out, lse), (_, rp, ci) = S.scale_forward(Q, K, V, scale_of(cfg), rho, out_dtype=out_dtype,
+                                               return_lse=True)
+    torch.cuda.synchronize()
+    lists = csr_rows(rp, ci)
+    nq = O.num_blocks(cfg.len_q, cfg.block)
+    sampler = None
+    if nsample:
+        def sampler(h):
+            rng = np.random.default_rng(1000 + h)
+            return sorted({0, nq - 1, *rng.choice(nq, nsample, replace=False).tolist()})
+    _check_attention(cfg, Q, K, V, lists, out, lse, range(cfg.heads) if heads is None else heads,
+                     sampler, cfg.dtype == "bf16")
+
+
+def test_bsa_end_to_end_against_oracle_selection():
+    """Where the selections agree, the GPU output meets the bounds against the oracle's own sets."""
+    cfg = I.S192P
+    print_case("bsa e2e", cfg.name)
+    Q, K, V = inputs(cfg)
+    out = S.scale_forward(Q, K, V, scale_of(cfg), 0.3)[0]
+    torch.cuda.synchronize()
+    for h in (0, 5):
+        res = O.scale_head(head_np(Q, h), head_np(K, h), head_np(V, h), cfg.len_text, cfg.len_ref,
+                           cfg.block, cfg.softmax_scale, 0.3)
+        mx, mean = attention_errors(to_f64(out[0, h]), res["out"])
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
+
+
+@pytest.mark.parametrize("cfg,heads,nsample", [(I.TINY, None, None), (I.S192P, [0, 15], 8)])
+def test_dense_parity(cfg, heads, nsample):
+    print_case("dense", cfg.name)
+    Q, K, V = inputs(cfg)
+    out, lse = S.dense_attn_fwd(Q, K, V, scale_of(cfg), out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    nq, nk = O.num_blocks(cfg.len_q, cfg.block), O.num_blocks(cfg.len_k, cfg.block)
+    lists = [np.arange(nk)] * (nq * cfg.heads)
+    sampler = None
+    if nsample:
+        def sampler(h):
+            rng = np.random.default_rng(7 + h)
+            return sorted({0, nq - 1, *rng.choice(nq, nsample, replace=False).tolist()})
+    _check_attention(cfg, Q, K, V, lists, out, lse, range(cfg.heads) if heads is None else heads,
+                     sampler, cfg.dtype == "bf16")
+
+
+@pytest.mark.parametrize("cfg", [I.TINY, I.S192P])
+def test_bsa_full_csr_equals_dense_bitwise(cfg):
+    print_case("full csr == dense", cfg.name)
+    Q, K, V = inputs(cfg)
+    sc = S.sparstar_pool_score(Q, K, scale_of(cfg))[2]
+    rp, ci = S.sparstar_select_blocks(sc, Q, K, scale_of(cfg), 1.0)
+    a = S.sparstar_bsa_fwd(Q, K, V, rp, ci, scale_of(cfg))
+    d = S.dense_attn_fwd(Q, K, V, scale_of(cfg))
+    torch.cuda.synchronize()
+    assert torch.equal(a, d)
+
+
+# ---------------------------------------------------------------- properties and edge cases
+
+def test_determinism_and_nan_poison():
+    cfg = I.S192P
+    print_case("determinism", cfg.name)
+    Q, K, V = inputs(cfg)
+    outs = []
+    for _ in range(2):
+        o = torch.full(Q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full(Q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+        _, _, sc = S.sparstar_pool_score(Q, K, scale_of(cfg))
+        rp, ci = S.sparstar_select_blocks(sc, Q, K, scale_of(cfg), 0.3)
+        res = S.sparstar_bsa_fwd(Q, K, V, rp, ci, scale_of(cfg), out=o, return_lse=True)
+        torch.cuda.synchronize()
+        assert not torch.isnan(res[0]).any() and not torch.isnan(res[1]).any()
+        outs.append((sc.clone(), rp.clone(), ci.clone(), res[0].clone(), res[1].clone()))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+def _custom_inputs(L_text, L_ref, L_q, H, D, dtype, seed=3):
+    g = torch.Generator().manual_seed(seed)
+    L_k = L_text + L_ref + L_q
+    Q = torch.randn((1, H, L_q, D), generator=g).to(dtype)
+    K = torch.randn((1, H, L_k, D), generator=g).to(dtype)
+    V = torch.randn((1, H, L_k, D), generator=g).to(dtype)
+    return Q.to(DEV), K.to(DEV), V.to(DEV)
+
+
+@pytest.mark.parametrize("L_text,L_ref,L_q,H,D,b,dtype,rho", [
+    (0, 37, 200, 2, 128, 128, torch.bfloat16, 0.5),     # no text, partial blocks, 1-token-odd tail
+    (100, 0, 129, 2, 128, 128, torch.bfloat16, 0.3),    # no reference; a 1-token query block
+    (512, 1000, 1000, 3, 128, 128, torch.bfloat16, 0.2),
+    (16, 256, 255, 2, 64, 64, torch.bfloat16, 0.5),     # float32 kernel with bf16 inputs
+    (7, 100, 300, 2, 128, 128, torch.float32, 0.4),     # float32 kernel, D = b = 128
+    (0, 0, 1, 1, 128, 128, torch.bfloat16, 1.0),        # a single token
+])
+def test_ragged_shapes(L_text, L_ref, L_q, H, D, b, dtype, rho):
+    print_case("ragged", L_text, L_ref, L_q, H, D, b, dtype, rho)
+    Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, D, dtype)
+    scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(D))
+    (out, lse), (sc, rp, ci) = S.scale_forward(Q, K, V, scale, rho, out_dtype=torch.float32,
+                                                 return_lse=True)
+    torch.cuda.synchronize()
+    lists = csr_rows(rp, ci)
+    nq = O.num_blocks(L_q, b)
+    for h in range(H):
+        q, k, v = head_np(Q, h), head_np(K, h), head_np(V, h)
+        res = O.scale_head(q, k, v, L_text, L_ref, b, 1 / math.sqrt(D), rho, rows=[])
+        for i in range(nq):
+            compare_row_selection(lists[h * nq + i], res["sets"][i], res["scores"][i],
+                                  len(res["retained"]), res["k"])
+        ref_o, ref_l = oracle_rows(q, k, v, lists[h * nq:(h + 1) * nq], range(nq), b, 1 / math.sqrt(D))
+        got = to_f64(out[0, h])
+        for i in range(nq):
+            s, e = O.block_range(i, L_q, b)
+            mx, _ = attention_errors(got[s:e], ref_o[i])
+            assert mx <= (BF16_MAX_ABS if dtype == torch.bfloat16 else F32_MAX_ABS), (h, i, mx)
+            assert np.max(np.abs(to_f64(lse[0, h])[s:e] - ref_l[i])) < 2e-3
+
+
+@pytest.mark.parametrize("D,b,dtype", [(128, 128, torch.bfloat16), (64, 64, torch.float32)])
+def test_irregular_csr(D, b, dtype):
+    """Uneven block lists: empty rows, one block, every block, duplicates and
+    out-of-range indices (skipped), rows in any order."""
+    L_text, L_ref, L_q, H = 64, 700, 600, 2
+    print_case("irregular csr", D, b, dtype)
+    Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, D, dtype, seed=11)
+    scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(D))
+    nq, nk = O.num_blocks(L_q, b), O.num_blocks(L_text + L_ref + L_q, b)
+    rng = np.random.default_rng(5)
+    lists = []
+    for r in range(H * nq):
+        kind = r % 6
+        if kind == 0:
+            lists.append(np.zeros(0, dtype=np.int64))
+        elif kind == 1:
+            lists.append(np.array([nk - 1]))
+        elif kind == 2:
+            lists.append(np.arange(nk)[::-1])
+        elif kind == 3:
+            lists.append(np.array([3, 3, 5]))
+        elif kind == 4:
+            lists.append(np.array([-1, 2, nk, 1000]))
+        else:
+            lists.append(rng.choice(nk, rng.integers(1, nk + 1), replace=False))
+    rp = np.zeros(len(lists) + 1, dtype=np.int32)
+    rp[1:] = np.cumsum([len(x) for x in lists])
+    ci = np.concatenate(lists).astype(np.int32)
+    out, lse = S.sparstar_bsa_fwd(Q, K, V, torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV),
+                                  scale, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    tol = BF16_MAX_ABS if dtype == torch.bfloat16 else F32_MAX_ABS
+    for h in range(H):
+        q, k, v = head_np(Q, h), head_np(K, h), head_np(V, h)
+        got, got_l = to_f64(out[0, h]), to_f64(lse[0, h])
+        for i in range(nq):
+            s, e = O.block_range(i, L_q, b)
+            blocks = [j for j in lists[h * nq + i] if 0 <= j < nk]
+            if not blocks:
+                assert np.all(got[s:e] == 0) and np.all(np.isneginf(got_l[s:e]))
+                continue
+            o_ref, l_ref, _ = O.attend_row(q[s:e], k, v, blocks, b, 1 / math.sqrt(D))
+            assert np.max(np.abs(got[s:e] - o_ref)) <= tol, (h, i)
+            assert np.max(np.abs(got_l[s:e] - l_ref)) < 2e-3
+
+
+def test_strided_views():
+    """Q/K/V as views into a packed [B, L, H, D] buffer and a strided output."""
+    cfg = I.TINY.with_(dtype="bf16", head_dim=128, block=128, grid=(2, 8, 16), ref_grid=(2, 8, 16))
+    print_case("strided", cfg.name)
+    Q, K, V = I.make_inputs(cfg, device=DEV)
+    Qp = Q.transpose(1, 2).contiguous().transpose(1, 2)    # [B,H,L,D] view of [B,L,H,D] memory
+    Kp = K.transpose(1, 2).contiguous().transpose(1, 2)
+    Vp = V.transpose(1, 2).contiguous().transpose(1, 2)
+    outp = torch.empty((1, cfg.len_q, cfg.heads, 128), dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    sc = scale_of(cfg)
+    ref = S.scale_forward(Q, K, V, sc, 0.5)[0]
+    _, _, scs = S.sparstar_pool_score(Qp, Kp, sc)
+    rp, ci = S.sparstar_select_blocks(scs, Qp, Kp, sc, 0.5)
+    S.sparstar_bsa_fwd(Qp, Kp, Vp, rp, ci, sc, out=outp)
+    torch.cuda.synchronize()
+    assert torch.equal(outp, ref)
+
+
+# ---------------------------------------------------------------- full size (sampled)
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg,rho", [(I.S720P, 0.2), (I.SWEEP[0], 0.2)])
+def test_full_size_sampled(cfg, rho):
+    """The timed launch configuration at full size: selection on every row of sampled heads,
+    attention on sampled query blocks (first, last partial, random)."""
+    print_case("full size", cfg.name, rho)
+    Q, K, V = inputs(cfg)
+    (out, lse), (sc, rp, ci) = S.scale_forward(Q, K, V, scale_of(cfg), rho, return_lse=True)
+    torch.cuda.synchronize()
+    lists = csr_rows(rp, ci)
+    b = cfg.block
+    nq = O.num_blocks(cfg.len_q, b)
+    heads = [0, cfg.heads - 1]
+    swaps = 0
+    for h in heads:
+        q, k = head_np(Q, h), head_np(K, h)
+        S_ref = O.block_scores(O.pool_blocks(q, b), O.pool_blocks(k, b), cfg.softmax_scale)
+        R, C = O.retained_and_candidates(cfg.len_text, cfg.len_ref, cfg.len_q, b)
+        kk = O.budget(len(C), rho)
+        ref_sets = O.select_blocks(S_ref, R, C, kk)
+        for i in range(nq):
+            swaps += compare_row_selection(lists[h * nq + i], ref_sets[i], S_ref[i], len(R), kk)
+    print(f"near-tie swaps over {len(heads) * nq} rows: {swaps}")
+
+    def sampler(h):
+        rng = np.random.default_rng(100 + h)
+        return sorted({0, nq - 1, *rng.choice(nq, 4, replace=False).tolist()})
+    _check_attention(cfg, Q, K, V, lists, out, lse, [0, 13, cfg.heads - 1], sampler, True)
