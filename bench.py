@@ -1,0 +1,288 @@
+"""Benchmark one SparSTAR scale on one MI355X.
+
+    python bench.py [--workload 720p] [--density 0.2] [--steps K] [--warmup W]
+
+A step is one pass of the whole hot path over one scale: sparstar_pool_score
+(block means + block scores), sparstar_select_blocks (per-row top-k -> CSR)
+and sparstar_bsa_fwd (block-sparse attention), on one stream, with the
+inputs already resident in HBM.  Prints one JSON line:
+
+  value        effective TFLOP/s over the executed blocks for the whole step
+               (4 * |B_i| * |B_j| * D per executed block pair, real tokens;
+               pooling, scoring and selection time included in the denominator)
+  ms_per_step  ms per scale
+  roofline     bsa_fwd (the dominant kernel) against bf16 MFMA peak, timed with
+               HIP events on the stream the kernels run on
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same scale,
+               extrapolated to the whole scale (a baseline, not a target)
+
+--dense times dense_attn_fwd instead (the density-1 baseline).  --gpus > 1
+is refused: this path runs on one GPU and shards by head with no exchange.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/scale and effective TFLOP/s (executed blocks) at 72k-token 720p scale"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsa_fwd_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_aggregated_amd", "csrc", "attn_mfma.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p",
+                    help="720p (default), 480p, 192p, tiny_f32, sweep, or a 720p_sweep_sN scale")
+    ap.add_argument("--density", type=float, default=None, help="default: 0.2 at 720p, else the workload's")
+    ap.add_argument("--out-dtype", choices=("bf16", "f32"), default=None)
+    ap.add_argument("--dense", action="store_true", help="time dense_attn_fwd (density 1 baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16, help="query blocks the oracle attends in its sample")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def workload_configs(name):
+    from block_sparse_attention_aggregated_amd import inputs as I
+    if name == "sweep":
+        return list(I.SWEEP)
+    return [I.WORKLOADS[name]]
+
+
+def exec_flops(cfg, row_ptr, col_idx) -> int:
+    """Executed-pair FLOPs from the CSR: 4 * |B_i| * |B_j| * D over real tokens."""
+    b = cfg.block
+    nq = -(-cfg.len_q // b)
+    nk = -(-cfg.len_k // b)
+    klen = np.minimum(b, cfg.len_k - np.arange(nk) * b).astype(np.int64)
+    qlen = np.minimum(b, cfg.len_q - np.arange(nq) * b).astype(np.int64)
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy().astype(np.int64)[:rp[-1]]
+    cs = np.concatenate([[0], np.cumsum(klen[ci])])
+    row_keys = cs[rp[1:]] - cs[rp[:-1]]
+    rows_q = np.tile(qlen, cfg.batch * cfg.heads)
+    return int(4 * cfg.head_dim * np.sum(rows_q * row_keys))
+
+
+def scoring_bytes(cfg) -> int:
+    """Algorithmic bytes of pool_score: read Q and K once, write the pooled blocks and scores."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    b = cfg.block
+    nq, nk = -(-cfg.len_q // b), -(-cfg.len_k // b)
+    BH = cfg.batch * cfg.heads
+    return BH * ((cfg.len_q + cfg.len_k) * cfg.head_dim * el + (nq + nk) * cfg.head_dim * 4 + nq * nk * 4)
+
+
+def traffic_record():
+    """Measured HBM bytes per bsa_fwd launch, if taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    return rec if rec.get("kernel_sha256") == src else None
+
+
+def cpu_baseline(cfg, density, Q, K, V, n_rows):
+    """Time the float64 oracle on one head's pooling/scoring/selection and n_rows query blocks
+    of attention, then extrapolate to the whole scale (all heads, all rows)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    b, sigma = cfg.block, cfg.softmax_scale
+    q = Q[0, 0].cpu().double().numpy()
+    k = K[0, 0].cpu().double().numpy()
+    v = V[0, 0].cpu().double().numpy()
+    t0 = time.perf_counter()
+    res = O.scale_head(q, k, v, cfg.len_text, cfg.len_ref, b, sigma, density, rows=[])
+    t_sel = time.perf_counter() - t0
+    nq = O.num_blocks(cfg.len_q, b)
+    rng = np.random.default_rng(0)
+    rows = sorted({0, nq - 1, *rng.choice(nq, max(0, n_rows - 2), replace=False).tolist()})[:max(n_rows, 1)]
+    t0 = time.perf_counter()
+    O.sparse_attention(q, k, v, res["sets"], b, sigma, rows=rows)
+    t_att = time.perf_counter() - t0
+    flops_rows = O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim,
+                                  [res["sets"][i] if i in rows else [] for i in range(nq)])
+    flops_head = O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim, res["sets"])
+    # extrapolate: selection per head x heads; attention by executed FLOPs
+    t_total = cfg.batch * cfg.heads * (t_sel + t_att * flops_head / max(flops_rows, 1))
+    flops_total = cfg.batch * cfg.heads * flops_head
+    return {
+        "value": flops_total / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "ms_per_scale_extrapolated": t_total * 1e3,
+        "sample": (f"float64 numpy oracle: pooling+scoring+selection of 1 of {cfg.heads} heads "
+                   f"({t_sel:.2f} s) and attention of {len(rows)} of {nq} query blocks of that head "
+                   f"({t_att:.2f} s), extrapolated to all heads and rows by executed FLOPs"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by head with "
+              "no exchange, so N GPUs would each run this same benchmark at H/N heads.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from block_sparse_attention_aggregated_amd import inputs as I
+    from block_sparse_attention_aggregated_amd import sparstar as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfgs = workload_configs(args.workload)
+    density = args.density if args.density is not None else (0.2 if args.workload in ("720p", "sweep")
+                                                            else cfgs[0].densities[0])
+    print(f"# generating {args.workload} inputs", file=sys.stderr, flush=True)
+    scales = []
+    for cfg in cfgs:
+        Q, K, V = I.make_inputs(cfg, device=dev)
+        od = {"bf16": torch.bfloat16, "f32": torch.float32, None: Q.dtype}[args.out_dtype]
+        sc = S.Scale(cfg.len_text, cfg.len_ref, cfg.block, cfg.softmax_scale)
+        qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
+        rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, density)
+        out = torch.empty(Q.shape, dtype=od, device=dev)
+        scales.append(dict(cfg=cfg, Q=Q, K=K, V=V, sc=sc, qp=qp, kp=kp, scores=scores, rp=rp, ci=ci, out=out))
+    torch.cuda.synchronize()
+    for s in scales:
+        s["flops"] = (4 * s["cfg"].head_dim * s["cfg"].batch * s["cfg"].heads * s["cfg"].len_q * s["cfg"].len_k
+                      if args.dense else exec_flops(s["cfg"], s["rp"], s["ci"]))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        for n, s in enumerate(scales):
+            if events is not None:
+                events[n][0].record(stream)
+            if args.dense:
+                S.dense_attn_fwd(s["Q"], s["K"], s["V"], s["sc"], out=s["out"])
+                if events is not None:
+                    events[n][1].record(stream)
+                    events[n][2].record(stream)
+            else:
+                S.sparstar_pool_score(s["Q"], s["K"], s["sc"], s["qp"], s["kp"], s["scores"])
+                if events is not None:
+                    events[n][1].record(stream)
+                S.sparstar_select_blocks(s["scores"], s["Q"], s["K"], s["sc"], density, row_ptr=s["rp"],
+                                         col_idx=s["ci"])
+                if events is not None:
+                    events[n][2].record(stream)
+                S.sparstar_bsa_fwd(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"])
+            if events is not None:
+                events[n][3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in scales] for _ in range(args.steps)]
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_scale = []
+    for n, s in enumerate(scales):
+        pool = np.array([e[n][0].elapsed_time(e[n][1]) for e in ev])
+        sel = np.array([e[n][1].elapsed_time(e[n][2]) for e in ev])
+        att = np.array([e[n][2].elapsed_time(e[n][3]) for e in ev])
+        tot = np.array([e[n][0].elapsed_time(e[n][3]) for e in ev])
+        cfg = s["cfg"]
+        per_scale.append({
+            "scale": cfg.name, "len_q": cfg.len_q, "len_k": cfg.len_k,
+            "ms_pool_score": float(pool.mean()), "ms_select": float(sel.mean()),
+            "ms_attention": float(att.mean()), "ms_attention_median": float(np.median(att)),
+            "ms_scale": float(tot.mean()),
+            "exec_tflop": s["flops"] / 1e12,
+            "attention_tflops": s["flops"] / (att.mean() * 1e-3) / 1e12,
+            "scoring_gbs": (scoring_bytes(cfg) / (pool.mean() * 1e-3) / 1e9) if not args.dense else None,
+        })
+    flops = sum(s["flops"] for s in scales)
+    ms_step = wall * 1e3 / args.steps      # bracketed by device synchronisation
+    ms_step_events = sum(p["ms_scale"] for p in per_scale)
+    att_ms = sum(p["ms_attention"] for p in per_scale)
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    traffic = traffic_record()
+    cfg0 = cfgs[-1]
+    rec = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg0.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian + sinusoidal (t,h,w) locality + 2 sink keys; stands in for "
+                "InfinityStar activations)",
+        "config": {
+            "workload": ("720p final scale: 72,000 queries, keys 512 text + 72,000 preceding-clip + "
+                         "72,000 current" if args.workload == "720p" else args.workload),
+            "heads": cfg0.heads, "head_dim": cfg0.head_dim, "block": cfg0.block, "density": density,
+            "mode": "dense" if args.dense else "sparse",
+            "out_dtype": str(scales[0]["out"].dtype).replace("torch.", ""),
+            "parallelism": "single GPU",
+        },
+        "ms_per_scale": ms_step / len(scales),
+        "event_ms_per_step": ms_step_events,
+        "scales": per_scale,
+        "roofline": {
+            "kernel": "dense_attn_fwd" if args.dense else "sparstar_bsa_fwd",
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": (traffic["bytes_per_launch"] if traffic and traffic.get("workload") == args.workload
+                        and abs(traffic.get("density", -1) - density) < 1e-12 and not args.dense else None),
+        },
+    }
+    if not args.dense and len(scales) == 1:
+        p = per_scale[0]
+        rec["scoring_roofline"] = {"kernel": "sparstar_pool_score", "bound": "hbm",
+                                   "achieved": p["scoring_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": p["scoring_gbs"] / PEAK_HBM_GBS,
+                                   "bytes": scoring_bytes(cfgs[0])}
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["calib_copy_bytes"] = 2 * n * 4
+    if not args.no_cpu_baseline and not args.dense:
+        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        s = scales[-1]
+        rec["cpu_baseline"] = cpu_baseline(s["cfg"], density, s["Q"], s["K"], s["V"], args.cpu_rows)
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

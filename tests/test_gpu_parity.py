@@ -14,7 +14,7 @@ from block_sparse_attention_aggregated_amd import inputs as I
 from block_sparse_attention_aggregated_amd import sparstar as S
 
 from parity import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, attention_errors, compare_row_selection,
-                    csr_rows, oracle_rows, to_f64)
+                    csr_rows, excess_over_bf16_store, oracle_rows, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,7 +119,8 @@ def test_select_parity_end_to_end(cfg, rho, heads):
 def _check_attention(cfg, Q, K, V, rows_lists, out, lse, heads, sample_rows, bf16_in):
     b, sigma = cfg.block, cfg.softmax_scale
     nq = O.num_blocks(cfg.len_q, b)
-    worst_max, sum_abs, n = 0.0, 0.0, 0
+    worst_max, worst_excess, sum_abs, n = 0.0, -1.0, 0.0, 0
+    bf16_store = out.dtype == torch.bfloat16
     for h in heads:
         q, k, v = head_np(Q, h), head_np(K, h), head_np(V, h)
         lists = rows_lists[h * nq:(h + 1) * nq]
@@ -131,14 +132,18 @@ def _check_attention(cfg, Q, K, V, rows_lists, out, lse, heads, sample_rows, bf1
             s, e = O.block_range(i, cfg.len_q, b)
             mx, mean = attention_errors(got[s:e], ref_o[i])
             worst_max = max(worst_max, mx)
+            if bf16_store:
+                worst_excess = max(worst_excess, excess_over_bf16_store(got[s:e], ref_o[i]))
             sum_abs += mean * (e - s) * cfg.head_dim
             n += (e - s) * cfg.head_dim
             if got_l is not None:
                 assert np.max(np.abs(got_l[s:e] - ref_l[i])) < (2e-3 if bf16_in else 1e-5), (h, i)
     mean_abs = sum_abs / max(n, 1)
-    print(f"max-abs {worst_max:.3e} mean-abs {mean_abs:.3e} over {n // cfg.head_dim} queries")
+    print(f"max-abs {worst_max:.3e} mean-abs {mean_abs:.3e} over {n // cfg.head_dim} queries"
+          + (f"; beyond the bf16 store rounding {worst_excess:.3e}" if bf16_store else ""))
     if bf16_in:
-        assert worst_max <= BF16_MAX_ABS and mean_abs <= BF16_MEAN_ABS
+        assert mean_abs <= BF16_MEAN_ABS
+        assert (worst_excess if bf16_store else worst_max) <= BF16_MAX_ABS
     else:
         assert worst_max <= F32_MAX_ABS
     return worst_max, mean_abs
@@ -179,8 +184,9 @@ def test_bsa_end_to_end_against_oracle_selection():
     for h in (0, 5):
         res = O.scale_head(head_np(Q, h), head_np(K, h), head_np(V, h), cfg.len_text, cfg.len_ref,
                            cfg.block, cfg.softmax_scale, 0.3)
-        mx, mean = attention_errors(to_f64(out[0, h]), res["out"])
-        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
+        got = to_f64(out[0, h])
+        mx, mean = attention_errors(got, res["out"])
+        assert excess_over_bf16_store(got, res["out"]) <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
 
 
 @pytest.mark.parametrize("cfg,heads,nsample", [(I.TINY, None, None), (I.S192P, [0, 15], 8)])
