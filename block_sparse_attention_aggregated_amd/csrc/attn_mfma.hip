@@ -24,15 +24,19 @@
 //     asked for, the unrounded sum is kept beside it for that output,
 //   O^T[d, query] += V^T P^T  16 MFMAs in four chains (A = V^T from LDS,
 //                             B = P straight from the S^T register layout).
-// While a sub-tile is computed, the next one is fetched: K straight into the
-// other LDS buffer with global_load_lds_dwordx4 (no registers), V into 16
-// registers, written to LDS transposed (v_perm 4 x 8 transposes) after the
-// P.V product.  V keys of each 16-key group are permuted so that a lane's
-// eight P values (keys 8*(r/4) + 4*half + r%4 of the S^T layout) meet the
-// matching eight V values in one 16-byte LDS read.  K rows (256 bytes) and
-// V^T rows (128 bytes) have XOR-swizzled 16-byte chunks: the MFMA operand
-// reads are free of bank conflicts without padding.  One barrier per sub-tile.
-// The block lists are read through the scalar cache.
+// Software pipeline: the S MFMAs of sub-tile t+1 are issued while the softmax
+// of sub-tile t runs, so K runs one sub-tile ahead of V.  K and V both go from
+// global memory straight into LDS with global_load_lds_dwordx4 (no registers):
+// the K of sub-tile t+2 and the V of sub-tile t+1 are fetched during step t.
+// V stays row-major in LDS; the V^T operand of the P.V MFMA is read with
+// ds_read_b64_tr_b16, which hands lane j of each 16-lane group element j&3 of
+// the 8-byte segments addressed by lanes (j>>2) + 4e: sixteen source lanes
+// pointing at 4 keys x 16 features deliver 16 features x 4 keys.  Two such
+// reads give a lane the eight keys 8*(r/4) + 4*half + r%4 that its P values
+// (the S^T layout) hold.  K and V rows (256 B) have XOR-swizzled 16-byte
+// chunks, chosen so that the MFMA operand reads of both are free of bank
+// conflicts without padding.  One barrier per sub-tile.  The block lists are
+// read through the scalar cache.
 //
 // Workgroups are mapped to rows XCD-aware: consecutive workgroup ids are
 // dispatched round-robin over the 8 XCDs, so row = (id % 8) * rows_per_xcd +
@@ -40,6 +44,8 @@
 // overlapping key-block lists hit the same L2.
 
 #include "sparstar_internal.h"
+
+#include <type_traits>
 
 namespace sparstar {
 namespace {
@@ -68,17 +74,21 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
 
 constexpr int SUB = 64;            // keys per LDS sub-tile (half a key block)
 
-// Chunk swizzles (16-byte chunks).  K rows are 256 bytes (16 chunks), V^T rows
-// 128 bytes (8 chunks of one 64-key sub-tile).
-__device__ inline int k_chunk(int row, int chunk) { return chunk ^ (row & 15); }
-__device__ inline int v_chunk(int d, int chunk) { return chunk ^ (((d >> 1) ^ (d >> 4)) & 7); }
+// LDS layout (bytes): two K sub-tile buffers [64 keys][256 B], then two V^T
+// sub-tile buffers [128 features][128 B].
+constexpr int kKBuf = SUB * HD * 2;    // 16 KB
+constexpr int kVBuf = SUB * HD * 2;    // 16 KB
+constexpr int kKOff0 = 0, kVOff0 = 2 * kKBuf;
+constexpr int kSmem = 2 * kKBuf + 2 * kVBuf;
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 template <bool kDense, bool kOutBf16, bool kLse>
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int rows_per_xcd) {
-  // Two buffers of one 64-key sub-tile each: K [64 keys][128 features] and
-  // V^T [128 features][64 key positions].
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][SUB * HD];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][HD * SUB];
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   const Geometry& g = a.g;
   const int64_t total_rows = (int64_t)g.B * g.H * g.n_q;
@@ -110,22 +120,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY, l = 0.f, l_exact = 0.f;  // l: sum of the bf16-rounded P; l_exact: unrounded
+  // l: sum of the bf16-rounded P (normalises O); l_exact: unrounded sum (for the LSE).
+  float m_run = -INFINITY, l = 0.f, l_exact = 0.f;
   const float c = a.sigma * kLog2e;
 
   // The block lists are read-only here: read them through the scalar cache.
   typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
   const cint_ptr rp = (cint_ptr)a.row_ptr;
   const cint_ptr ci = (cint_ptr)a.col_idx;
-  int64_t beg = 0, end = g.n_k;
+  // List positions fit in 32 bits: row_ptr entries are int32.
+  int beg = 0, end = g.n_k;
   if (!kDense) {
     beg = rp[row];
     end = rp[row + 1];
     if (beg < 0) beg = 0;
-    if (end > a.col_idx_len) end = a.col_idx_len;
+    if ((int64_t)end > a.col_idx_len) end = (int)a.col_idx_len;
   }
-  auto col = [&](int64_t p) -> int { return kDense ? (int)p : ci[p]; };
-  auto next_valid = [&](int64_t p) -> int64_t {
+  auto next_valid = [&](int p) -> int {
     if (!kDense) {
       while (p < end) {
         const int j = ci[p];
@@ -135,135 +146,158 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     }
     return p;
   };
-  // Real keys in sub-tile h of block j (<= 0: the sub-tile is empty).
-  auto sub_len = [&](int j, int h) -> int {
-    return (int)min<int64_t>(SUB, g.L_k - (int64_t)j * BK - (int64_t)h * SUB);
+  // A sub-tile: half h of key block j at list position p; len real keys (1..64).
+  struct Sub {
+    int p, j, h, len;
+  };
+  auto make_sub = [&](int p, int h) -> Sub {
+    Sub s;
+    s.p = p;
+    s.h = h;
+    s.j = p < end ? (kDense ? (int)p : ci[p]) : 0;
+    s.len = p < end ? min(SUB, (int)g.L_k - s.j * BK - h * SUB) : 0;
+    return s;
+  };
+  auto advance = [&](const Sub& s) -> Sub {
+    if (s.p >= end) return s;
+    if (s.h == 0 && (int)g.L_k - s.j * BK > SUB) return make_sub(s.p, 1);
+    return make_sub(next_valid(s.p + 1), 0);
   };
 
-  // K staging (direct to LDS): wavefront w, round t fills rows 16t + 4w .. +4 of a
-  // sub-tile; lane i writes row +i/16, physical chunk i%16, i.e. logical chunk
-  // (i%16) ^ (row%16) of that key.
-  const int k_row_in_round = 4 * wave + (lane >> 4);
-  const int k_lchunk = (lane & 15) ^ (k_row_in_round & 15);
-  const int64_t k_thr = ((int64_t)k_row_in_round * a.ks_t + k_lchunk * 8) * 2;   // bytes
-  const int64_t k_round = (int64_t)16 * a.ks_t * 2;                                  // bytes per round
-  // V staging (registers): keys 4*kg .. +4 of the sub-tile, features 8*fg .. +8.
-  const int fg = tid & 15, kg = tid >> 4;
-  const int64_t v_thr = ((int64_t)(4 * kg) * a.vs_t + fg * 8) * 2;                   // bytes
-  const int v_s = kg >> 2, v_a = (kg & 3) >> 1, v_hh = kg & 1;
-  uint4 vst[4];
+  // K and V staging (direct to LDS): wavefront w, round t (0..3) fills rows
+  // 16t + 4w .. +4 of a sub-tile; lane i writes row +i/16 at physical chunk i%16.
+  // K rows hold logical chunk c at physical chunk c ^ (row & 15); V rows at
+  // c ^ (2 * (row & 7)).
+  const int st_row0 = 4 * wave + (lane >> 4);  // row in round 0; round t adds 16t
+  // In-head byte offsets fit in 32 bits (the host routes larger layouts elsewhere).
+  const uint32_t ks_b = (uint32_t)a.ks_t * 2u, vs_b = (uint32_t)a.vs_t * 2u;  // bytes per key
+  const uint32_t k_thr = (uint32_t)st_row0 * ks_b + (uint32_t)(((lane & 15) ^ (st_row0 & 15)) * 16);
+  const uint32_t v_thr = (uint32_t)st_row0 * vs_b + (uint32_t)(((lane & 15) ^ (2 * (st_row0 & 7))) * 16);
 
-  auto issue_loads = [&](int j, int h, int buf) {
-    const int len = sub_len(j, h);
-    const int64_t key0 = (int64_t)j * BK + h * SUB;
-    const char* kblk = kbase + key0 * a.ks_t * 2;
-    const char* vblk = vbase + key0 * a.vs_t * 2;
-    char* kdst = reinterpret_cast<char*>(&Ks[buf][0]);
+  // LDS read offsets.  K: row kt*32 + l32, logical chunk 2ks + hl, physical chunk
+  // (2ks + hl) ^ (row & 15) = 2ks ^ (hl ^ (l32 & 15)); kt adds 32 rows.
+  const uint32_t k_row = l32 * (HD * 2), k_sw = hl ^ (l32 & 15);
+  // V^T operand by transposing reads.  Lane L = 16g + m points at key
+  // 16ks + 8r + 4(g >> 1) + (m >> 2) (r = 0, 1 for the two reads of a step) and
+  // features 32dt + 16(g & 1) + 4(m & 3) .. +4: chunk 4dt + cc, cc = 2(g & 1) + (m & 3) / 2,
+  // byte 8 (m & 1) in it; physical chunk (4dt + cc) ^ 2kr with kr = 4(g >> 1) + (m >> 2)
+  // (keys 16ks + 8r + kr share row & 7), i.e. (cc ^ 2kr) ^ 4dt.
+  uint32_t v_tr[HD / 32];
+  {
+    const int g16 = lane >> 4, m16 = lane & 15;
+    const int kr = 4 * (g16 >> 1) + (m16 >> 2);
+    const int cx = (2 * (g16 & 1) + ((m16 & 3) >> 1)) ^ (2 * kr);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = 16 * t + k_row_in_round;
-      const char* src = kblk + (r < len ? t * k_round + k_thr : (int64_t)(lane & 15) * 16);
-      char* dst = kdst + (16 * t + 4 * wave) * (HD * 2);  // wave-uniform LDS base of this round
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           (uint32_t)(uintptr_t)dst),
-                                       16, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = 4 * kg + e;
-      vst[e] = ld16(vblk + (key < len ? (int64_t)e * a.vs_t * 2 + v_thr : (int64_t)fg * 16));
-    }
-  };
-
-  auto store_v = [&](int len, int buf) {
-    if (len < SUB) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * kg + e >= len) vst[e] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint4 x = vst[e];
-        w[e] = (dd >> 1) == 0 ? x.x : (dd >> 1) == 1 ? x.y : (dd >> 1) == 2 ? x.z : x.w;
-      }
-      uint2 outv;
-      outv.x = __builtin_amdgcn_perm(w[1], w[0], sel);
-      outv.y = __builtin_amdgcn_perm(w[3], w[2], sel);
-      const int d = fg * 8 + dd;
-      *reinterpret_cast<uint2*>(&Vt[buf][d * SUB + v_chunk(d, 2 * v_s + v_hh) * 8 + 4 * v_a]) = outv;
-    }
-  };
-
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  int64_t p = next_valid(beg);
-  int h = 0, buf = 0;
-  if (p < end) {
-    issue_loads(col(p), 0, 0);
-    store_v(sub_len(col(p), 0), 0);
+    for (int dt = 0; dt < HD / 32; ++dt)
+      v_tr[dt] = (uint32_t)(kr * (HD * 2) + ((cx ^ (4 * dt)) << 4) + 8 * (m16 & 1));
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 
-#pragma unroll 1
-  while (p < end) {
-    const int j = col(p);
-    const int len = sub_len(j, h);
-    // Next sub-tile: the second half of this block if it has keys, else the next block.
-    int64_t pn = p;
-    int hn = 1;
-    if (h == 1 || sub_len(j, 1) <= 0) {
-      pn = next_valid(p + 1);
-      hn = 0;
-    }
-    const bool has_next = pn < end;
-    int jn = 0;
-    if (has_next) {
-      jn = col(pn);
-      issue_loads(jn, hn, buf ^ 1);
-    }
-
-    // S^T = K Q^T: two independent 32-key tiles, eight steps of 16 features.
-    f32x16 s[SUB / 32];
+  // Rows past the end of a partial sub-tile read row 0 instead: their scores are
+  // masked to -inf, so their probabilities are exactly 0 and the P.V product adds
+  // 0 times a real, finite V row.
+  auto load_tile = [&](const char* base, uint32_t stride_b, uint32_t thr, const Sub& s, int off, bool is_v) {
+    const char* blk = base + (uint32_t)(s.j * BK + s.h * SUB) * stride_b;
+    const uint32_t ldsb = (uint32_t)(uintptr_t)(smem + off + 4 * wave * (HD * 2));
+    if (s.len == SUB) {
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks) {
-      bf16x8 kf[SUB / 32];
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + t * 16u * stride_b + thr),
+                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                             ldsb + t * 16 * (HD * 2)),
+                                         16, 0, 0);
+    } else {
 #pragma unroll
-      for (int kt = 0; kt < SUB / 32; ++kt) {
-        const int r = kt * 32 + l32;
-        kf[kt] = as_bf16x8(ld16(&Ks[buf][r * HD + k_chunk(r, ks * 2 + hl) * 8]));
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + st_row0;
+        const uint32_t src_off = r < s.len ? t * 16u * stride_b + thr
+                                           : (uint32_t)(((lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15))) * 16);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + src_off),
+                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                             ldsb + t * 16 * (HD * 2)),
+                                         16, 0, 0);
       }
+    }
+  };
+  auto load_k = [&](const Sub& s, int off) { load_tile(kbase, ks_b, k_thr, s, off, false); };
+  auto load_v = [&](const Sub& s, int off) { load_tile(vbase, vs_b, v_thr, s, off, true); };
+  auto k_frag = [&](int koff, int kt, int ks) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(smem + koff + kt * 32 * (HD * 2) + k_row +
+                                                      (((2 * ks) ^ k_sw) << 4)));
+  };
+  auto v_frag = [&](int voff, int dt, int ks) -> bf16x8 {
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const uint32_t base = (uint32_t)(uintptr_t)(smem + voff + ks * 16 * (HD * 2)) + v_tr[dt];
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(base));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(base + 8 * (HD * 2)));
+    bf16x8 r;
+    __builtin_memcpy(&r, &lo, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
+    return r;
+  };
+  // S^T of one sub-tile from K buffer koff (two 32-key tiles, eight 16-feature steps).
+  auto compute_s = [&](int koff, f32x16 (&s)[SUB / 32]) {
+#pragma unroll
+    for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
       for (int kt = 0; kt < SUB / 32; ++kt) {
+        const bf16x8 kf = k_frag(koff, kt, ks);
         if (ks == 0) {
           f32x16 z;
 #pragma unroll
           for (int r = 0; r < 16; ++r) z[r] = 0.f;
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt], qf[ks], z, 0, 0, 0);
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], z, 0, 0, 0);
         } else {
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt], qf[ks], s[kt], 0, 0, 0);
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
         }
       }
-    }
-    if (len < SUB) {
+  };
+
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // S of the current and the next sub-tile; the two arrays swap roles every step.
+  f32x16 sA[SUB / 32], sB[SUB / 32];
+
+  // Prologue: sub-tiles c0 (K and V), c1 (K) in flight; S of c0.
+  Sub cur = make_sub(next_valid(beg), 0);
+  Sub nxt = advance(cur);
+  if (cur.p < end) {
+    load_k(cur, kKOff0);
+    load_v(cur, kVOff0);
+    if (nxt.p < end) load_k(nxt, kKOff0 + kKBuf);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (cur.p < end) compute_s(kKOff0, sA);
+  __syncthreads();
+
+  // One pipeline step for the sub-tile with sequence parity PAR: its K was in
+  // K buffer PAR, its V is in V buffer PAR; the next sub-tile's K is in K buffer
+  // PAR ^ 1.  During the step: the K of the sub-tile after next goes to K buffer
+  // PAR, the next V to V buffer PAR ^ 1.
+  auto step = [&](auto par) {
+    constexpr int PAR = decltype(par)::value;
+    constexpr int kOffCur = kKOff0 + PAR * kKBuf, kOffNxt = kKOff0 + (PAR ^ 1) * kKBuf;
+    constexpr int vOffCur = kVOff0 + PAR * kVBuf, vOffNxt = kVOff0 + (PAR ^ 1) * kVBuf;
+    f32x16(&s_cur)[SUB / 32] = PAR == 0 ? sA : sB;
+    f32x16(&s_nxt)[SUB / 32] = PAR == 0 ? sB : sA;
+    const Sub nn = advance(nxt);
+    if (nn.p < end) load_k(nn, kOffCur);
+    if (nxt.p < end) load_v(nxt, vOffNxt);
+
+    // Softmax statistics of the current sub-tile.
+    if (cur.len < SUB) {
 #pragma unroll
       for (int kt = 0; kt < SUB / 32; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (key >= len) s[kt][r] = -INFINITY;
+          if (key >= cur.len) s_cur[kt][r] = -INFINITY;
         }
     }
-    // Sub-tile max, lazy update of the reference max.
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < SUB / 32; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const bool need = (mx - m_run) * c > kTau;
     if (__any(need)) {
@@ -279,13 +313,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     }
     const float mc = m_run * c;
 
-    // P = exp2(s*c - m*c) in bf16, laid out as the B operand of the P.V MFMA; row
-    // sums over the rounded values with v_dot2.
+    // Interleaved: S of the next sub-tile (MFMA) with P of this one (VALU).
+    compute_s(kOffNxt, s_nxt);
     bf16x8 pf[SUB / 16];
-    float rs[SUB / 32];
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < SUB / 32; ++kt) {
-      rs[kt] = 0.f;
+    for (int kt = 0; kt < SUB / 32; ++kt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         union {
@@ -295,37 +328,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           f32x2 f;
-          f[0] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * hh + 2 * e], c, -mc));
-          f[1] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * hh + 2 * e + 1], c, -mc));
+          f[0] = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][8 * hh + 2 * e], c, -mc));
+          f[1] = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][8 * hh + 2 * e + 1], c, -mc));
           if (kLse) l_exact += f[0] + f[1];
           pu.q[e] = __builtin_convertvector(f, bf16x2);
-          rs[kt] = __builtin_amdgcn_fdot2_f32_bf16(pu.q[e], ones, rs[kt], false);
+          if (kt == 0) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[e], ones, rs0, false);
+          else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[e], ones, rs1, false);
         }
         pf[kt * 2 + hh] = pu.v;
       }
+    // 16 x (1 K read, 1 MFMA, 6 VALU of the softmax).
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
     }
-    l += rs[0] + rs[1];
+    l += rs0 + rs1;
 
-    // O^T += V^T P^T: four independent 32-feature tiles, four steps of 16 keys.
+    // O^T += V^T P^T: 16 (dt, ks) steps, two transposing reads each.
 #pragma unroll
-    for (int ks = 0; ks < SUB / 16; ++ks) {
-      bf16x8 vf[HD / 32];
-#pragma unroll
-      for (int dt = 0; dt < HD / 32; ++dt) {
-        const int d = dt * 32 + l32;
-        vf[dt] = as_bf16x8(ld16(&Vt[buf][d * SUB + v_chunk(d, ks * 2 + hl) * 8]));
-      }
+    for (int ks = 0; ks < SUB / 16; ++ks)
 #pragma unroll
       for (int dt = 0; dt < HD / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[ks], o[dt], 0, 0, 0);
-    }
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vOffCur, dt, ks), pf[ks], o[dt], 0, 0, 0);
 
-    if (has_next) store_v(sub_len(jn, hn), buf ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS K writes of the next sub-tile have landed
+    __builtin_amdgcn_s_waitcnt(0);  // the K and V of later sub-tiles have landed in LDS
     __syncthreads();
-    p = pn;
-    h = hn;
-    buf ^= 1;
+    cur = nxt;
+    nxt = nn;
+  };
+
+#pragma unroll 1
+  while (cur.p < end) {
+    step(std::integral_constant<int, 0>());
+    if (cur.p >= end) break;
+    step(std::integral_constant<int, 1>());
   }
 
   // Epilogue: the two lanes of a query hold partial row sums of disjoint keys.

@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -188,7 +189,10 @@ sparstar_status run_attn(const sparstar::AttnArgs& a, hipStream_t st) {
   if (rows == 0) return ok();
   sparstar_status s = check_device();
   if (s != SPARSTAR_OK) return s;
-  const bool mfma = a.dtype == SPARSTAR_BF16 && a.g.D == 128 && a.g.b == 128;
+  // The MFMA kernel keeps in-head byte offsets in 32 bits.
+  const bool small_extent = (a.g.L_k + 128) * std::max(a.ks_t, a.vs_t) * 2 < ((int64_t)1 << 31) &&
+                            (a.g.L_q + 128) * std::max(a.qs_t, a.os_t) * 4 < ((int64_t)1 << 31);
+  const bool mfma = a.dtype == SPARSTAR_BF16 && a.g.D == 128 && a.g.b == 128 && small_extent;
   return launched(mfma ? sparstar::launch_attn_mfma(a, st) : sparstar::launch_attn_simt(a, st),
                   mfma ? "attention (bf16 MFMA) launch" : "attention (float32) launch");
 }
