@@ -14,20 +14,26 @@
 //                             LDS, B = Q held in registers for the whole row),
 //   online softmax in float32 registers: the MFMA output layout gives each
 //     lane one query and 16 keys per 32-key tile, so the row max is an in-lane
-//     max3 reduction plus one exchange with lane ^ 32; exp2 with sigma*log2(e)
-//     folded into one FMA.  The reference max is only raised when a sub-tile's
-//     max exceeds it by more than 2^8 (in exp2 units), so the rescale of the
-//     output accumulators is rare; probabilities stay below 2^8.
+//     max3 reduction plus one v_permlane32_swap with lane ^ 32; exp2 with
+//     sigma*log2(e) folded into one FMA.  The reference max is only raised when
+//     a sub-tile's max exceeds it by more than 2^8 (in exp2 units), so the
+//     rescale of the output accumulators is rare; probabilities stay below 2^8.
 //   P is rounded to bf16 once, and the row sum used to normalise O is taken
 //     over those rounded values with v_dot2 (two per instruction), so the
 //     weights the MFMA sees are normalised by their own sum; when the LSE is
 //     asked for, the unrounded sum is kept beside it for that output,
 //   O^T[d, query] += V^T P^T  16 MFMAs in four chains (A = V^T from LDS,
 //                             B = P straight from the S^T register layout).
-// Software pipeline: the S MFMAs of sub-tile t+1 are issued while the softmax
-// of sub-tile t runs, so K runs one sub-tile ahead of V.  K and V both go from
-// global memory straight into LDS with global_load_lds_dwordx4 (no registers):
-// the K of sub-tile t+2 and the V of sub-tile t+1 are fetched during step t.
+// Software pipeline, one step per sub-tile t, in two explicitly ordered phases:
+//   phase 1: the S MFMAs of sub-tile t+1, each beside the exp2 / convert / sum
+//            of two probabilities of sub-tile t;
+//   phase 2: the P.V MFMAs of sub-tile t, each beside a max3 over two scores of
+//            sub-tile t+1 (its row max, needed at the start of the next step).
+// LDS operand fragments are read two MFMAs ahead of their use.  K and V go
+// from global memory straight into LDS with buffer_load_dwordx4 ... lds (no
+// registers): the K of sub-tile t+2 and the V of sub-tile t+1 are fetched
+// during step t, into four separately declared LDS buffers so that the
+// compiler need not wait for them before reading the other buffers.
 // V stays row-major in LDS; the V^T operand of the P.V MFMA is read with
 // ds_read_b64_tr_b16, which hands lane j of each 16-lane group element j&3 of
 // the 8-byte segments addressed by lanes (j>>2) + 4e: sixteen source lanes
@@ -74,21 +80,29 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
 
 constexpr int SUB = 64;            // keys per LDS sub-tile (half a key block)
 
-// LDS layout (bytes): two K sub-tile buffers [64 keys][256 B], then two V^T
-// sub-tile buffers [128 features][128 B].
-constexpr int kKBuf = SUB * HD * 2;    // 16 KB
-constexpr int kVBuf = SUB * HD * 2;    // 16 KB
-constexpr int kKOff0 = 0, kVOff0 = 2 * kKBuf;
-constexpr int kSmem = 2 * kKBuf + 2 * kVBuf;
-
-// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+// LDS: two K and two V sub-tile buffers, each [64 keys][256 B] row-major.  They
+// are four separate objects, and every LDS address below is derived from one of
+// them, so the compiler can tell that a read of one buffer does not depend on
+// the direct-to-LDS loads still in flight into another.
+constexpr int kTile = SUB * HD * 2;    // 16 KB
+typedef __attribute__((address_space(3))) char lds_char;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// s_waitcnt immediate (gfx9 encoding) that waits for lgkmcnt == 0 only:
+// vmcnt = 63 (bits 3:0 and 15:14), expcnt = 7 (bits 6:4), lgkmcnt = 0 (bits 11:8).
+constexpr int kWaitLgkm0 = 0xC07F;
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+
 template <bool kDense, bool kOutBf16, bool kLse>
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int rows_per_xcd) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ __attribute__((aligned(16))) char k_lds0[kTile];
+  __shared__ __attribute__((aligned(16))) char k_lds1[kTile];
+  __shared__ __attribute__((aligned(16))) char v_lds0[kTile];
+  __shared__ __attribute__((aligned(16))) char v_lds1[kTile];
+  lds_char* const kb[2] = {(lds_char*)k_lds0, (lds_char*)k_lds1};
+  lds_char* const vb[2] = {(lds_char*)v_lds0, (lds_char*)v_lds1};
 
   const Geometry& g = a.g;
   const int64_t total_rows = (int64_t)g.B * g.H * g.n_q;
@@ -195,38 +209,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   // Rows past the end of a partial sub-tile read row 0 instead: their scores are
   // masked to -inf, so their probabilities are exactly 0 and the P.V product adds
   // 0 times a real, finite V row.
-  auto load_tile = [&](const char* base, uint32_t stride_b, uint32_t thr, const Sub& s, int off, bool is_v) {
-    const char* blk = base + (uint32_t)(s.j * BK + s.h * SUB) * stride_b;
-    const uint32_t ldsb = (uint32_t)(uintptr_t)(smem + off + 4 * wave * (HD * 2));
+  // K and V go through buffer resources (base = this head's first row, range =
+  // its extent): the direct-to-LDS buffer load keeps the compiler's LDS waits
+  // exact (a direct-to-LDS global load would turn every LDS wait issued while it
+  // is in flight into lgkmcnt(0)).  The sub-tile's first row is the scalar offset.
+  const uint32_t k_extent = (uint32_t)(((int64_t)g.L_k - 1) * a.ks_t * 2 + HD * 2);
+  const uint32_t v_extent = (uint32_t)(((int64_t)g.L_k - 1) * a.vs_t * 2 + HD * 2);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)k_extent, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)v_extent, kBufferFlags);
+  auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t stride_b, uint32_t thr, const Sub& s,
+                       lds_char* buf, bool is_v) {
+    const uint32_t soff = (uint32_t)(s.j * BK + s.h * SUB) * stride_b;
+    lds_char* const ldsb = buf + 4 * wave * (HD * 2);
     if (s.len == SUB) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + t * 16u * stride_b + thr),
-                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                             ldsb + t * 16 * (HD * 2)),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 16 * (HD * 2), 16, t * 16u * stride_b + thr, soff,
+                                                 0, 0);
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + st_row0;
         const uint32_t src_off = r < s.len ? t * 16u * stride_b + thr
                                            : (uint32_t)(((lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15))) * 16);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + src_off),
-                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                             ldsb + t * 16 * (HD * 2)),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 16 * (HD * 2), 16, src_off, soff, 0, 0);
       }
     }
   };
-  auto load_k = [&](const Sub& s, int off) { load_tile(kbase, ks_b, k_thr, s, off, false); };
-  auto load_v = [&](const Sub& s, int off) { load_tile(vbase, vs_b, v_thr, s, off, true); };
-  auto k_frag = [&](int koff, int kt, int ks) -> bf16x8 {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(smem + koff + kt * 32 * (HD * 2) + k_row +
-                                                      (((2 * ks) ^ k_sw) << 4)));
+  auto load_k = [&](const Sub& s, lds_char* buf) { load_tile(k_rsrc, ks_b, k_thr, s, buf, false); };
+  auto load_v = [&](const Sub& s, lds_char* buf) { load_tile(v_rsrc, vs_b, v_thr, s, buf, true); };
+  auto k_frag = [&](lds_char* buf, int kt, int ks) -> bf16x8 {
+    typedef const __attribute__((address_space(3))) bf16x8* lds_bf16x8;
+    return *(lds_bf16x8)(buf + kt * 32 * (HD * 2) + k_row + (((2 * ks) ^ k_sw) << 4));
   };
-  auto v_frag = [&](int voff, int dt, int ks) -> bf16x8 {
+  auto v_frag = [&](lds_char* buf, int dt, int ks) -> bf16x8 {
     typedef __attribute__((address_space(3))) v4s* lds_v4s;
-    const uint32_t base = (uint32_t)(uintptr_t)(smem + voff + ks * 16 * (HD * 2)) + v_tr[dt];
+    lds_char* const base = buf + ks * 16 * (HD * 2) + v_tr[dt];
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(base));
     const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(base + 8 * (HD * 2)));
     bf16x8 r;
@@ -234,74 +254,87 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
     return r;
   };
-  // S^T of one sub-tile from K buffer koff (two 32-key tiles, eight 16-feature steps).
-  auto compute_s = [&](int koff, f32x16 (&s)[SUB / 32]) {
+  // S^T of one sub-tile from K buffer buf (two 32-key tiles, eight 16-feature
+  // steps); used once, before the pipelined loop.
+  auto compute_s = [&](lds_char* buf, f32x16 (&s)[SUB / 32]) {
 #pragma unroll
     for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < SUB / 32; ++kt) {
-        const bf16x8 kf = k_frag(koff, kt, ks);
-        if (ks == 0) {
-          f32x16 z;
+      for (int kt = 0; kt < SUB / 32; ++kt)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(buf, kt, ks), qf[ks], ks == 0 ? f32x16{} : s[kt],
+                                                        0, 0, 0);
+  };
+  // Scores of keys past the end of a partial sub-tile become -inf.
+  auto mask_tail = [&](f32x16 (&s)[SUB / 32], int len) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) z[r] = 0.f;
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], z, 0, 0, 0);
-        } else {
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
-        }
+    for (int kt = 0; kt < SUB / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+        if (key >= len) s[kt][r] = -INFINITY;
       }
+  };
+  // Max over the two lanes that hold one query (lane and lane ^ 32).
+  auto pair_max = [](float x) -> float {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto tile_max = [&](const f32x16 (&s)[SUB / 32]) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < SUB / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+    return pair_max(mx);
   };
 
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   // S of the current and the next sub-tile; the two arrays swap roles every step.
   f32x16 sA[SUB / 32], sB[SUB / 32];
 
-  // Prologue: sub-tiles c0 (K and V), c1 (K) in flight; S of c0.
+  // Prologue: sub-tiles c0 (K and V), c1 (K) in flight; S of c0 and its max.
   Sub cur = make_sub(next_valid(beg), 0);
   Sub nxt = advance(cur);
   if (cur.p < end) {
-    load_k(cur, kKOff0);
-    load_v(cur, kVOff0);
-    if (nxt.p < end) load_k(nxt, kKOff0 + kKBuf);
+    load_k(cur, kb[0]);
+    load_v(cur, vb[0]);
+    if (nxt.p < end) load_k(nxt, kb[1]);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (cur.p < end) compute_s(kKOff0, sA);
+  float mx_cur = -INFINITY;
+  if (cur.p < end) {
+    compute_s(kb[0], sA);
+    if (cur.len < SUB) mask_tail(sA, cur.len);
+    mx_cur = tile_max(sA);
+  }
   __syncthreads();
 
-  // One pipeline step for the sub-tile with sequence parity PAR: its K was in
-  // K buffer PAR, its V is in V buffer PAR; the next sub-tile's K is in K buffer
-  // PAR ^ 1.  During the step: the K of the sub-tile after next goes to K buffer
-  // PAR, the next V to V buffer PAR ^ 1.
+  // One pipeline step for the sub-tile with sequence parity PAR.  On entry: its
+  // S and max are in registers, its V is in V buffer PAR and the next sub-tile's
+  // K in K buffer PAR ^ 1.  The step fetches the K of the sub-tile after next
+  // into K buffer PAR and the next V into V buffer PAR ^ 1, then runs two
+  // explicitly ordered phases (sched_barrier keeps the order):
+  //   phase 1: 16 MFMAs of S(next), each beside the softmax of two P values of
+  //            this sub-tile; K fragments are read two MFMAs ahead;
+  //   phase 2: 16 MFMAs of O += V^T P^T, each beside a max3 over two scores of
+  //            S(next); V fragments are read two MFMAs ahead.
   auto step = [&](auto par) {
     constexpr int PAR = decltype(par)::value;
-    constexpr int kOffCur = kKOff0 + PAR * kKBuf, kOffNxt = kKOff0 + (PAR ^ 1) * kKBuf;
-    constexpr int vOffCur = kVOff0 + PAR * kVBuf, vOffNxt = kVOff0 + (PAR ^ 1) * kVBuf;
+    lds_char* const k_cur = kb[PAR];
+    lds_char* const k_nxt = kb[PAR ^ 1];
+    lds_char* const v_cur = vb[PAR];
+    lds_char* const v_nxt = vb[PAR ^ 1];
     f32x16(&s_cur)[SUB / 32] = PAR == 0 ? sA : sB;
     f32x16(&s_nxt)[SUB / 32] = PAR == 0 ? sB : sA;
     const Sub nn = advance(nxt);
-    if (nn.p < end) load_k(nn, kOffCur);
-    if (nxt.p < end) load_v(nxt, vOffNxt);
+    if (nn.p < end) load_k(nn, k_cur);
+    if (nxt.p < end) load_v(nxt, v_nxt);
 
-    // Softmax statistics of the current sub-tile.
-    if (cur.len < SUB) {
-#pragma unroll
-      for (int kt = 0; kt < SUB / 32; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (key >= cur.len) s_cur[kt][r] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < SUB / 32; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = (mx - m_run) * c > kTau;
+    // Raise the reference max only where this sub-tile exceeds it by more than kTau.
+    const bool need = (mx_cur - m_run) * c > kTau;
     if (__any(need)) {
-      const float m_new = need ? mx : m_run;
+      const float m_new = need ? mx_cur : m_run;
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       l *= alpha;
       if (kLse) l_exact *= alpha;
@@ -313,45 +346,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     }
     const float mc = m_run * c;
 
-    // Interleaved: S of the next sub-tile (MFMA) with P of this one (VALU).
-    compute_s(kOffNxt, s_nxt);
-    bf16x8 pf[SUB / 16];
+    // Phase 1.  MFMA i: key tile i & 1, feature step i >> 1.  P values 2i, 2i + 1
+    // (tile i >> 3, registers 2(i & 7), +1) form pair i & 3 of P operand i >> 2.
+    // Drain the scalar loads of the block list first: their returns are unordered,
+    // and with none pending every LDS wait below counts only the LDS reads ahead
+    // of it (lgkmcnt(n) rather than lgkmcnt(0)).  vmcnt and expcnt: no wait.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    bf16x8 kf[3], vf[3];
+    kf[0] = k_frag(k_nxt, 0, 0);
+    kf[1] = k_frag(k_nxt, 1, 0);
+    union {
+      bf16x8 v[SUB / 16];
+      bf16x2 q[SUB / 4];
+    } pu;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < SUB / 32; ++kt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        union {
-          bf16x8 v;
-          bf16x2 q[4];
-        } pu;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f32x2 f;
-          f[0] = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][8 * hh + 2 * e], c, -mc));
-          f[1] = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][8 * hh + 2 * e + 1], c, -mc));
-          if (kLse) l_exact += f[0] + f[1];
-          pu.q[e] = __builtin_convertvector(f, bf16x2);
-          if (kt == 0) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[e], ones, rs0, false);
-          else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[e], ones, rs1, false);
-        }
-        pf[kt * 2 + hh] = pu.v;
-      }
-    // 16 x (1 K read, 1 MFMA, 6 VALU of the softmax).
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) kf[(i + 2) % 3] = k_frag(k_nxt, (i + 2) & 1, (i + 2) >> 1);
+      else vf[i - 14] = v_frag(v_cur, i - 14, 0);
+      const int kt = i & 1, ks = i >> 1;
+      s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], ks == 0 ? f32x16{} : s_nxt[kt], 0,
+                                                          0, 0);
+      const int t = i >> 3, r = 2 * (i & 7);
+      f32x2 f;
+      f[0] = __builtin_amdgcn_exp2f(fmaf(s_cur[t][r], c, -mc));
+      f[1] = __builtin_amdgcn_exp2f(fmaf(s_cur[t][r + 1], c, -mc));
+      if (kLse) l_exact += f[0] + f[1];
+      pu.q[i] = __builtin_convertvector(f, bf16x2);
+      if (t == 0) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs0, false);
+      else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs1, false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Keep the softmax above in phase 1: without this, the compiler sinks it past
+    // the branch below, next to its first use.
+    asm volatile("" : "+v"(pu.v[0]), "+v"(pu.v[1]), "+v"(pu.v[2]), "+v"(pu.v[3]), "+v"(rs0), "+v"(rs1));
+    l += rs0 + rs1;
+    if (nxt.len < SUB) mask_tail(s_nxt, nxt.len);
+
+    // Phase 2.  MFMA i: feature tile i & 3, key step i >> 2.
+    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+      if (i + 2 < 16) vf[(i + 2) % 3] = v_frag(v_cur, (i + 2) & 3, (i + 2) >> 2);
+      const int dt = i & 3, ks = i >> 2;
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pu.v[ks], o[dt], 0, 0, 0);
+      const int t = i >> 3, r = 2 * (i & 7);
+      mx = fmaxf(mx, fmaxf(s_nxt[t][r], s_nxt[t][r + 1]));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    l += rs0 + rs1;
-
-    // O^T += V^T P^T: 16 (dt, ks) steps, two transposing reads each.
-#pragma unroll
-    for (int ks = 0; ks < SUB / 16; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < HD / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vOffCur, dt, ks), pf[ks], o[dt], 0, 0, 0);
+    mx_cur = pair_max(mx);
 
     __builtin_amdgcn_s_waitcnt(0);  // the K and V of later sub-tiles have landed in LDS
     __syncthreads();
