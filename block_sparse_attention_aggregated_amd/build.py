@@ -27,6 +27,9 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extra flags.  The attention kernel assumes NaN-free scores so that its
+# row max is plain v_max3 (IEEE-mode fmax would first quiet every operand).
+EXTRA = {"attn_mfma.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -40,7 +43,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *lang, *COMMON, *DEVICE, "-c", path, "-o", obj]
+    cmd = [hipcc(), *lang, *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

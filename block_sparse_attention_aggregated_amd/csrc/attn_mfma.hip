@@ -13,11 +13,12 @@
 //                             two independent accumulator chains (A = K from
 //                             LDS, B = Q held in registers for the whole row),
 //   online softmax in float32 registers: the MFMA output layout gives each
-//     lane one query and 16 keys per 32-key tile, so the row max is an in-lane
-//     max3 reduction plus one v_permlane32_swap with lane ^ 32; exp2 with
-//     sigma*log2(e) folded into one FMA.  The reference max is only raised when
-//     a sub-tile's max exceeds it by more than 2^8 (in exp2 units), so the
-//     rescale of the output accumulators is rare; probabilities stay below 2^8.
+//     lane one query and 16 keys per 32-key tile; exp2 with sigma*log2(e)
+//     folded into one FMA.  The softmax is optimistic: P is formed against the
+//     current reference max without computing the sub-tile's own max; the
+//     reference (the max of the first sub-tile) is only raised, with a rescale
+//     of O and the sums, when a lane's P sum reaches 2^64 (row max: in-lane
+//     max3 reduction plus one v_permlane32_swap with lane ^ 32).
 //   P is rounded to bf16 once, and the row sum used to normalise O is taken
 //     over those rounded values with v_dot2 (two per instruction), so the
 //     weights the MFMA sees are normalised by their own sum; when the LSE is
@@ -27,8 +28,7 @@
 // Software pipeline, one step per sub-tile t, in two explicitly ordered phases:
 //   phase 1: the S MFMAs of sub-tile t+1, each beside the exp2 / convert / sum
 //            of two probabilities of sub-tile t;
-//   phase 2: the P.V MFMAs of sub-tile t, each beside a max3 over two scores of
-//            sub-tile t+1 (its row max, needed at the start of the next step).
+//   phase 2: the P.V MFMAs of sub-tile t.
 // LDS operand fragments are read two MFMAs ahead of their use.  K and V go
 // from global memory straight into LDS with buffer_load_dwordx4 ... lds (no
 // registers): the K of sub-tile t+2 and the V of sub-tile t+1 are fetched
@@ -67,7 +67,7 @@ constexpr int HD = 128;            // head_dim
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTau = 8.0f;       // lazy-rescale threshold, exp2 units
+constexpr float kBig = 18446744073709551616.0f;  // 2^64: bound on a lane's P sum per sub-tile
 
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   const int64_t bh = row / g.n_q;
   const int qi = (int)(row - bh * g.n_q);
   const int bi = (int)(bh / g.H), hi = (int)(bh - (int64_t)bi * g.H);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int l32 = lane & 31, hl = lane >> 5;
 
   const __bf16* qbase = static_cast<const __bf16*>(a.q) + bi * a.qs_b + hi * a.qs_h;
@@ -181,12 +182,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   // K and V staging (direct to LDS): wavefront w, round t (0..3) fills rows
   // 16t + 4w .. +4 of a sub-tile; lane i writes row +i/16 at physical chunk i%16.
   // K rows hold logical chunk c at physical chunk c ^ (row & 15); V rows at
-  // c ^ (2 * (row & 7)).
+  // c ^ 4(row & 3), which moves whole 64-byte groups (the 32-feature slices).
   const int st_row0 = 4 * wave + (lane >> 4);  // row in round 0; round t adds 16t
   // In-head byte offsets fit in 32 bits (the host routes larger layouts elsewhere).
   const uint32_t ks_b = (uint32_t)a.ks_t * 2u, vs_b = (uint32_t)a.vs_t * 2u;  // bytes per key
   const uint32_t k_thr = (uint32_t)st_row0 * ks_b + (uint32_t)(((lane & 15) ^ (st_row0 & 15)) * 16);
-  const uint32_t v_thr = (uint32_t)st_row0 * vs_b + (uint32_t)(((lane & 15) ^ (2 * (st_row0 & 7))) * 16);
+  const uint32_t v_thr = (uint32_t)st_row0 * vs_b + (uint32_t)(((lane & 15) ^ (4 * (st_row0 & 3))) * 16);
 
   // LDS read offsets.  K: row kt*32 + l32, logical chunk 2ks + hl, physical chunk
   // (2ks + hl) ^ (row & 15) = 2ks ^ (hl ^ (l32 & 15)); kt adds 32 rows.
@@ -194,13 +195,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   // V^T operand by transposing reads.  Lane L = 16g + m points at key
   // 16ks + 8r + 4(g >> 1) + (m >> 2) (r = 0, 1 for the two reads of a step) and
   // features 32dt + 16(g & 1) + 4(m & 3) .. +4: chunk 4dt + cc, cc = 2(g & 1) + (m & 3) / 2,
-  // byte 8 (m & 1) in it; physical chunk (4dt + cc) ^ 2kr with kr = 4(g >> 1) + (m >> 2)
-  // (keys 16ks + 8r + kr share row & 7), i.e. (cc ^ 2kr) ^ 4dt.
+  // byte 8 (m & 1) in it; physical chunk (4dt + cc) ^ 4(kr & 3) with kr = 4(g >> 1) + (m >> 2)
+  // (keys 16ks + 8r + kr share row & 3), i.e. (cc ^ 4(kr & 3)) ^ 4dt.  The 32 lanes
+  // one LDS cycle serves (g = 0, 1, or 2, 3) read 4 keys x 32 features, whose four
+  // 64-byte groups land in the four distinct group slots of the 256-byte bank
+  // window: no bank conflicts.
   uint32_t v_tr[HD / 32];
   {
     const int g16 = lane >> 4, m16 = lane & 15;
     const int kr = 4 * (g16 >> 1) + (m16 >> 2);
-    const int cx = (2 * (g16 & 1) + ((m16 & 3) >> 1)) ^ (2 * kr);
+    const int cx = (2 * (g16 & 1) + ((m16 & 3) >> 1)) ^ (4 * (kr & 3));
 #pragma unroll
     for (int dt = 0; dt < HD / 32; ++dt)
       v_tr[dt] = (uint32_t)(kr * (HD * 2) + ((cx ^ (4 * dt)) << 4) + 8 * (m16 & 1));
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
       for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + st_row0;
         const uint32_t src_off = r < s.len ? t * 16u * stride_b + thr
-                                           : (uint32_t)(((lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15))) * 16);
+                                           : (uint32_t)(((lane & 15) ^ (is_v ? 4 * (r & 3) : (r & 15))) * 16);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 16 * (HD * 2), 16, src_off, soff, 0, 0);
       }
     }
@@ -264,15 +268,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(buf, kt, ks), qf[ks], ks == 0 ? f32x16{} : s[kt],
                                                         0, 0, 0);
   };
-  // Scores of keys past the end of a partial sub-tile become -inf.
+  // Scores of keys past the end of a partial sub-tile become -inf.  Register r of
+  // tile kt holds key kt*32 + 8(r/4) + 4hl + r%4; the lane part moves into the limit
+  // so that the per-register part stays an immediate.
   auto mask_tail = [&](f32x16 (&s)[SUB / 32], int len) {
+    const int lim = len - 4 * hl;
 #pragma unroll
     for (int kt = 0; kt < SUB / 32; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-        if (key >= len) s[kt][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (kt * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[kt][r] = -INFINITY;
   };
   // Max over the two lanes that hold one query (lane and lane ^ 32).
   auto pair_max = [](float x) -> float {
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
 #pragma unroll
     for (int kt = 0; kt < SUB / 32; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kt][r]), s[kt][r + 1]);
     return pair_max(mx);
   };
 
@@ -292,7 +297,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   // S of the current and the next sub-tile; the two arrays swap roles every step.
   f32x16 sA[SUB / 32], sB[SUB / 32];
 
-  // Prologue: sub-tiles c0 (K and V), c1 (K) in flight; S of c0 and its max.
+  // Prologue: sub-tiles c0 (K and V), c1 (K) in flight; S of c0.  The reference
+  // max starts at the max of c0.
   Sub cur = make_sub(next_valid(beg), 0);
   Sub nxt = advance(cur);
   if (cur.p < end) {
@@ -302,23 +308,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  float mx_cur = -INFINITY;
   if (cur.p < end) {
     compute_s(kb[0], sA);
     if (cur.len < SUB) mask_tail(sA, cur.len);
-    mx_cur = tile_max(sA);
+    m_run = tile_max(sA);
   }
   __syncthreads();
 
+  // Probabilities of one sub-tile against the reference max (mc = m_run * c):
+  // pair i of the P operands from scores 2i, 2i + 1, plus the row sums.
+  union PTile {
+    bf16x8 v[SUB / 16];
+    bf16x2 q[SUB / 4];
+  };
+  auto p_pair = [&](const f32x16 (&s)[SUB / 32], int i, float mc, PTile& pu, float& rs0, float& rs1, float& le) {
+    const int t = i >> 3, r = 2 * (i & 7);
+    f32x2 f;
+    f[0] = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mc));
+    f[1] = __builtin_amdgcn_exp2f(fmaf(s[t][r + 1], c, -mc));
+    if (kLse) le += f[0] + f[1];
+    pu.q[i] = __builtin_convertvector(f, bf16x2);
+    if (t == 0) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs0, false);
+    else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs1, false);
+  };
+
   // One pipeline step for the sub-tile with sequence parity PAR.  On entry: its
-  // S and max are in registers, its V is in V buffer PAR and the next sub-tile's
-  // K in K buffer PAR ^ 1.  The step fetches the K of the sub-tile after next
-  // into K buffer PAR and the next V into V buffer PAR ^ 1, then runs two
-  // explicitly ordered phases (sched_barrier keeps the order):
+  // S is in registers, its V is in V buffer PAR and the next sub-tile's K in K
+  // buffer PAR ^ 1.  The step fetches the K of the sub-tile after next into K
+  // buffer PAR and the next V into V buffer PAR ^ 1, then runs two explicitly
+  // ordered phases (sched_barrier keeps the order):
   //   phase 1: 16 MFMAs of S(next), each beside the softmax of two P values of
   //            this sub-tile; K fragments are read two MFMAs ahead;
-  //   phase 2: 16 MFMAs of O += V^T P^T, each beside a max3 over two scores of
-  //            S(next); V fragments are read two MFMAs ahead.
+  //   phase 2: 16 MFMAs of O += V^T P^T; V fragments are read two MFMAs ahead.
+  // The softmax is optimistic: P is computed against the current reference max
+  // without looking at this sub-tile's max.  Only if a lane's sum of the new P
+  // reaches 2^64 (so some P may be large, or infinite) is the sub-tile redone:
+  // its max (over both lanes of the query) becomes the reference, O and the sums
+  // are rescaled, and P is recomputed.  Below that bound every P < 2^64, and O
+  // and the sums (at most 2^17 keys) stay far inside the float32 range; the
+  // normalisation by the sum at the end is unchanged by the choice of reference.
   auto step = [&](auto par) {
     constexpr int PAR = decltype(par)::value;
     lds_char* const k_cur = kb[PAR];
@@ -330,20 +358,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     const Sub nn = advance(nxt);
     if (nn.p < end) load_k(nn, k_cur);
     if (nxt.p < end) load_v(nxt, v_nxt);
-
-    // Raise the reference max only where this sub-tile exceeds it by more than kTau.
-    const bool need = (mx_cur - m_run) * c > kTau;
-    if (__any(need)) {
-      const float m_new = need ? mx_cur : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      l *= alpha;
-      if (kLse) l_exact *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m_run = m_new;
-    }
     const float mc = m_run * c;
 
     // Phase 1.  MFMA i: key tile i & 1, feature step i >> 1.  P values 2i, 2i + 1
@@ -355,11 +369,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     bf16x8 kf[3], vf[3];
     kf[0] = k_frag(k_nxt, 0, 0);
     kf[1] = k_frag(k_nxt, 1, 0);
-    union {
-      bf16x8 v[SUB / 16];
-      bf16x2 q[SUB / 4];
-    } pu;
-    float rs0 = 0.f, rs1 = 0.f;
+    PTile pu;
+    float rs0 = 0.f, rs1 = 0.f, le_t = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 2 < 16) kf[(i + 2) % 3] = k_frag(k_nxt, (i + 2) & 1, (i + 2) >> 1);
@@ -367,34 +378,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
       const int kt = i & 1, ks = i >> 1;
       s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], ks == 0 ? f32x16{} : s_nxt[kt], 0,
                                                           0, 0);
-      const int t = i >> 3, r = 2 * (i & 7);
-      f32x2 f;
-      f[0] = __builtin_amdgcn_exp2f(fmaf(s_cur[t][r], c, -mc));
-      f[1] = __builtin_amdgcn_exp2f(fmaf(s_cur[t][r + 1], c, -mc));
-      if (kLse) l_exact += f[0] + f[1];
-      pu.q[i] = __builtin_convertvector(f, bf16x2);
-      if (t == 0) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs0, false);
-      else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs1, false);
+      p_pair(s_cur, i, mc, pu, rs0, rs1, le_t);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Keep the softmax above in phase 1: without this, the compiler sinks it past
-    // the branch below, next to its first use.
+    // the branches below, next to its first use.
     asm volatile("" : "+v"(pu.v[0]), "+v"(pu.v[1]), "+v"(pu.v[2]), "+v"(pu.v[3]), "+v"(rs0), "+v"(rs1));
+    if (__any(rs0 + rs1 >= kBig)) {
+      const float m_new = fmaxf(m_run, tile_max(s_cur));
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l *= alpha;
+      if (kLse) l_exact *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_run = m_new;
+      rs0 = rs1 = le_t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p_pair(s_cur, i, m_run * c, pu, rs0, rs1, le_t);
+    }
     l += rs0 + rs1;
+    if (kLse) l_exact += le_t;
     if (nxt.len < SUB) mask_tail(s_nxt, nxt.len);
 
     // Phase 2.  MFMA i: feature tile i & 3, key step i >> 2.
-    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 2 < 16) vf[(i + 2) % 3] = v_frag(v_cur, (i + 2) & 3, (i + 2) >> 2);
       const int dt = i & 3, ks = i >> 2;
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pu.v[ks], o[dt], 0, 0, 0);
-      const int t = i >> 3, r = 2 * (i & 7);
-      mx = fmaxf(mx, fmaxf(s_nxt[t][r], s_nxt[t][r + 1]));
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx_cur = pair_max(mx);
 
     __builtin_amdgcn_s_waitcnt(0);  // the K and V of later sub-tiles have landed in LDS
     __syncthreads();
