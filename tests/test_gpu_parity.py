@@ -331,6 +331,45 @@ def test_irregular_csr(D, b, dtype):
             assert np.max(np.abs(got_l[s:e] - l_ref)) < LSE_BF16
 
 
+@pytest.mark.parametrize("order", ["rising", "falling"])
+def test_bsa_reference_max_jumps(order):
+    """Key blocks whose scores sit far above those of the first block a row
+    visits (by up to ~10^3 in exp2 units, enough to overflow exp2 against the
+    first block's max), so the kernel must raise its reference max and rescale
+    mid-row; and the mirror case where the first block holds the largest
+    scores.  Output and LSE against the oracle."""
+    L_text, L_ref, L_q, H, D, b = 0, 896, 256, 2, 128, 128
+    print_case("max jumps", order)
+    g = torch.Generator().manual_seed(23)
+    L_k = L_text + L_ref + L_q
+    Q = torch.randn((1, H, L_q, D), generator=g)
+    K = torch.randn((1, H, L_k, D), generator=g)
+    V = torch.randn((1, H, L_k, D), generator=g)
+    gains = ([1.0, 1.0, 4.0, 1.0, 16.0, 2.0, 64.0, 1.0, 1.0] if order == "rising"   # per key block
+             else [64.0, 16.0, 4.0, 2.0, 1.0, 1.0, 1.0, 1.0, 1.0])
+    for j, gj in enumerate(gains):
+        K[:, :, j * b:(j + 1) * b] *= gj
+    Q, K, V = (t.to(torch.bfloat16).to(DEV) for t in (Q, K, V))
+    scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(D))
+    nq, nk = O.num_blocks(L_q, b), O.num_blocks(L_k, b)
+    lists = [np.arange(nk) for _ in range(H * nq)]
+    rp = np.zeros(len(lists) + 1, dtype=np.int32)
+    rp[1:] = np.cumsum([len(x) for x in lists])
+    ci = np.concatenate(lists).astype(np.int32)
+    out, lse = S.sparstar_bsa_fwd(Q, K, V, torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV),
+                                  scale, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    for h in range(H):
+        q, k, v = head_np(Q, h), head_np(K, h), head_np(V, h)
+        got, got_l = to_f64(out[0, h]), to_f64(lse[0, h])
+        for i in range(nq):
+            s, e = O.block_range(i, L_q, b)
+            o_ref, l_ref, _ = O.attend_row(q[s:e], k, v, list(range(nk)), b, 1 / math.sqrt(D))
+            assert np.max(np.abs(got[s:e] - o_ref)) <= BF16_MAX_ABS, (h, i)
+            # logits up to ~200: float32 dot products of length 128 with |k| up to ~256
+            assert np.max(np.abs(got_l[s:e] - l_ref)) < 2e-2
+
+
 def test_strided_views():
     """Q/K/V as views into a packed [B, L, H, D] buffer and a strided output."""
     cfg = I.TINY.with_(dtype="bf16", head_dim=128, block=128, grid=(2, 8, 16), ref_grid=(2, 8, 16))
