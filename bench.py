@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--out-dtype", choices=("bf16", "f32"), default=None)
     ap.add_argument("--dense", action="store_true", help="time dense_attn_fwd (density 1 baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=16, help="query blocks the oracle attends in its sample")
+    ap.add_argument("--cpu-rows", type=int, default=16,
+                    help="query blocks per head the oracle attends in its sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--json-out", default=None)
@@ -101,9 +102,11 @@ def traffic_record():
     return rec if rec.get("kernel_sha256") == src else None
 
 
-def cpu_baseline(cfg, density, Q, K, V, n_rows):
-    """Time the float64 oracle on one head's pooling/scoring/selection and n_rows query blocks
-    of attention, then extrapolate to the whole scale (all heads, all rows)."""
+def cpu_baseline(cfg, density, Q, K, V, rows_per_head):
+    """Time the float64 oracle on a bounded sample of the scale: pooling, scoring and
+    selection of every head, and attention of rows_per_head query blocks per head
+    (first, last and seeded random ones); the attention time is extrapolated to all
+    rows by executed FLOPs.  About 10-20 s of CPU work at 720p."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -111,30 +114,36 @@ def cpu_baseline(cfg, density, Q, K, V, n_rows):
     except Exception:
         cores = 1
     b, sigma = cfg.block, cfg.softmax_scale
-    q = Q[0, 0].cpu().double().numpy()
-    k = K[0, 0].cpu().double().numpy()
-    v = V[0, 0].cpu().double().numpy()
-    t0 = time.perf_counter()
-    res = O.scale_head(q, k, v, cfg.len_text, cfg.len_ref, b, sigma, density, rows=[])
-    t_sel = time.perf_counter() - t0
     nq = O.num_blocks(cfg.len_q, b)
     rng = np.random.default_rng(0)
-    rows = sorted({0, nq - 1, *rng.choice(nq, max(0, n_rows - 2), replace=False).tolist()})[:max(n_rows, 1)]
-    t0 = time.perf_counter()
-    O.sparse_attention(q, k, v, res["sets"], b, sigma, rows=rows)
-    t_att = time.perf_counter() - t0
-    flops_rows = O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim,
-                                  [res["sets"][i] if i in rows else [] for i in range(nq)])
-    flops_head = O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim, res["sets"])
-    # extrapolate: selection per head x heads; attention by executed FLOPs
-    t_total = cfg.batch * cfg.heads * (t_sel + t_att * flops_head / max(flops_rows, 1))
-    flops_total = cfg.batch * cfg.heads * flops_head
+    t_sel = t_att = 0.0
+    flops_rows = flops_all = 0
+    n_rows = 0
+    for bi in range(cfg.batch):
+        for h in range(cfg.heads):
+            q = Q[bi, h].cpu().double().numpy()
+            k = K[bi, h].cpu().double().numpy()
+            v = V[bi, h].cpu().double().numpy()
+            t0 = time.perf_counter()
+            res = O.scale_head(q, k, v, cfg.len_text, cfg.len_ref, b, sigma, density, rows=[])
+            t_sel += time.perf_counter() - t0
+            pick = rng.choice(nq, max(0, min(nq, rows_per_head) - 2), replace=False).tolist()
+            rows = sorted({0, nq - 1, *pick})[:max(rows_per_head, 1)]
+            t0 = time.perf_counter()
+            O.sparse_attention(q, k, v, res["sets"], b, sigma, rows=rows)
+            t_att += time.perf_counter() - t0
+            n_rows += len(rows)
+            flops_rows += O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim,
+                                           [res["sets"][i] if i in rows else [] for i in range(nq)])
+            flops_all += O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim, res["sets"])
+    t_total = t_sel + t_att * flops_all / max(flops_rows, 1)
     return {
-        "value": flops_total / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "value": flops_all / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
         "ms_per_scale_extrapolated": t_total * 1e3,
-        "sample": (f"float64 numpy oracle: pooling+scoring+selection of 1 of {cfg.heads} heads "
-                   f"({t_sel:.2f} s) and attention of {len(rows)} of {nq} query blocks of that head "
-                   f"({t_att:.2f} s), extrapolated to all heads and rows by executed FLOPs"),
+        "sample": (f"float64 numpy oracle on the same inputs: pooling+scoring+selection of all "
+                   f"{cfg.batch * cfg.heads} heads ({t_sel:.1f} s) and attention of {n_rows} of "
+                   f"{cfg.batch * cfg.heads * nq} query blocks ({rows_per_head} per head: first, last, "
+                   f"seeded random; {t_att:.1f} s), attention extrapolated to all rows by executed FLOPs"),
     }
 
 
@@ -277,6 +286,7 @@ def main():
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         s = scales[-1]
         rec["cpu_baseline"] = cpu_baseline(s["cfg"], density, s["Q"], s["K"], s["V"], args.cpu_rows)
+        print(f"# oracle sample: {rec['cpu_baseline']['sample']}", file=sys.stderr, flush=True)
     line = json.dumps(rec)
     print(line, flush=True)
     if args.json_out:
