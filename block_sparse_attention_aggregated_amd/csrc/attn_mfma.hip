@@ -44,10 +44,14 @@
 // conflicts without padding.  One barrier per sub-tile.  The block lists are
 // read through the scalar cache.
 //
-// Workgroups are mapped to rows XCD-aware: consecutive workgroup ids are
-// dispatched round-robin over the 8 XCDs, so row = (id % 8) * rows_per_xcd +
-// id / 8 keeps consecutive query blocks of one head on one XCD, where their
-// overlapping key-block lists hit the same L2.
+// Workgroups are mapped to rows XCD-aware.  Consecutive workgroup ids are
+// dispatched round-robin over the 8 XCDs; XCD x takes query blocks
+// [x * per_xcd, (x + 1) * per_xcd) of each head, per_xcd = ceil(n_q / 8), and
+// all XCDs go through the heads in the same order.  The workgroups resident on
+// one XCD are then consecutive query blocks of one head, whose block lists
+// overlap and share that XCD's L2; and at any time the whole GPU works on one
+// or two heads, whose K and V fit the Infinity Cache, so L2 misses are served
+// there rather than by HBM.
 
 #include "sparstar_internal.h"
 
@@ -96,7 +100,7 @@ constexpr int kWaitLgkm0 = 0xC07F;
 constexpr int kBufferFlags = 0x00020000;
 
 template <bool kDense, bool kOutBf16, bool kLse>
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int rows_per_xcd) {
+__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int per_xcd) {
   __shared__ __attribute__((aligned(16))) char k_lds0[kTile];
   __shared__ __attribute__((aligned(16))) char k_lds1[kTile];
   __shared__ __attribute__((aligned(16))) char v_lds0[kTile];
@@ -105,12 +109,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   lds_char* const vb[2] = {(lds_char*)v_lds0, (lds_char*)v_lds1};
 
   const Geometry& g = a.g;
-  const int64_t total_rows = (int64_t)g.B * g.H * g.n_q;
-  const int64_t row = (int64_t)(blockIdx.x % kXcds) * rows_per_xcd + blockIdx.x / kXcds;
-  if (row >= total_rows) return;  // uniform over the workgroup
-
-  const int64_t bh = row / g.n_q;
-  const int qi = (int)(row - bh * g.n_q);
+  // Workgroup id -> (head, query block): XCD x = id % 8 takes query blocks
+  // [x * per_xcd, (x + 1) * per_xcd) of every head, heads in order.
+  const int64_t k = blockIdx.x / kXcds;
+  const int64_t bh = k / per_xcd;
+  const int qi = (int)(blockIdx.x % kXcds) * per_xcd + (int)(k - bh * per_xcd);
+  if (qi >= g.n_q) return;  // uniform over the workgroup
+  const int64_t row = bh * g.n_q + qi;
   const int bi = (int)(bh / g.H), hi = (int)(bh - (int64_t)bi * g.H);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
@@ -457,18 +462,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
 }
 
 template <bool kDense, bool kOutBf16, bool kLse>
-void launch(const AttnArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.g.B * a.g.H * a.g.n_q;
-  const int rows_per_xcd = (int)((rows + kXcds - 1) / kXcds);
-  const int64_t grid = (int64_t)rows_per_xcd * kXcds;
+hipError_t launch(const AttnArgs& a, hipStream_t s) {
+  const int per_xcd = (a.g.n_q + kXcds - 1) / kXcds;
+  const int64_t grid = (int64_t)a.g.B * a.g.H * per_xcd * kXcds;
+  if (grid > 0xffffffffll) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_mfma_kernel<kDense, kOutBf16, kLse>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                     rows_per_xcd);
+                     per_xcd);
+  return hipSuccess;
 }
 
 template <bool kDense, bool kOutBf16>
-void launch2(const AttnArgs& a, hipStream_t s) {
-  if (a.lse) launch<kDense, kOutBf16, true>(a, s);
-  else launch<kDense, kOutBf16, false>(a, s);
+hipError_t launch2(const AttnArgs& a, hipStream_t s) {
+  return a.lse ? launch<kDense, kOutBf16, true>(a, s) : launch<kDense, kOutBf16, false>(a, s);
 }
 
 }  // namespace
@@ -477,9 +482,9 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.g.D != HD || a.g.b != BQ || a.dtype != 0) return hipErrorInvalidValue;
   const bool dense = a.row_ptr == nullptr;
   const bool ob = a.out_dtype == 0;
-  if (dense) ob ? launch2<true, true>(a, s) : launch2<true, false>(a, s);
-  else ob ? launch2<false, true>(a, s) : launch2<false, false>(a, s);
-  return hipGetLastError();
+  const hipError_t e = dense ? (ob ? launch2<true, true>(a, s) : launch2<true, false>(a, s))
+                             : (ob ? launch2<false, true>(a, s) : launch2<false, false>(a, s));
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace sparstar
