@@ -376,6 +376,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     kf[1] = k_frag(k_nxt, 1, 0);
     PTile pu;
     float rs0 = 0.f, rs1 = 0.f, le_t = 0.f;
+    // The softmax of pair i runs in three stages over three iterations (FMA in
+    // i - 2, exp2 in i - 1, convert and sum in i), so no instruction waits on the
+    // one issued just before it.
+    auto st_a = [&](int i) -> f32x2 {
+      const int t = i >> 3, r = 2 * (i & 7);
+      f32x2 x;
+      x[0] = fmaf(s_cur[t][r], c, -mc);
+      x[1] = fmaf(s_cur[t][r + 1], c, -mc);
+      return x;
+    };
+    auto st_b = [&](f32x2 x) -> f32x2 {
+      f32x2 e;
+      e[0] = __builtin_amdgcn_exp2f(x[0]);
+      e[1] = __builtin_amdgcn_exp2f(x[1]);
+      return e;
+    };
+    f32x2 x_1 = st_a(1), e_0 = st_b(st_a(0));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 2 < 16) kf[(i + 2) % 3] = k_frag(k_nxt, (i + 2) & 1, (i + 2) >> 1);
@@ -383,7 +400,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
       const int kt = i & 1, ks = i >> 1;
       s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], ks == 0 ? f32x16{} : s_nxt[kt], 0,
                                                           0, 0);
-      p_pair(s_cur, i, mc, pu, rs0, rs1, le_t);
+      const f32x2 x_2 = i + 2 < 16 ? st_a(i + 2) : f32x2{};
+      const f32x2 e_1 = i + 1 < 16 ? st_b(x_1) : f32x2{};
+      if (kLse) le_t += e_0[0] + e_0[1];
+      pu.q[i] = __builtin_convertvector(e_0, bf16x2);
+      if (i < 8) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs0, false);
+      else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs1, false);
+      e_0 = e_1;
+      x_1 = x_2;
       __builtin_amdgcn_sched_barrier(0);
     }
     // Keep the softmax above in phase 1: without this, the compiler sinks it past
