@@ -215,40 +215,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
       v_tr[dt] = (uint32_t)(kr * (HD * 2) + ((cx ^ (4 * dt)) << 4) + 8 * (m16 & 1));
   }
 
-  // Rows past the end of a partial sub-tile read row 0 instead: their scores are
-  // masked to -inf, so their probabilities are exactly 0 and the P.V product adds
-  // 0 times a real, finite V row.
-  // K and V go through buffer resources (base = this head's first row, range =
-  // its extent): the direct-to-LDS buffer load keeps the compiler's LDS waits
-  // exact (a direct-to-LDS global load would turn every LDS wait issued while it
-  // is in flight into lgkmcnt(0)).  The sub-tile's first row is the scalar offset.
-  const uint32_t k_extent = (uint32_t)(((int64_t)g.L_k - 1) * a.ks_t * 2 + HD * 2);
-  const uint32_t v_extent = (uint32_t)(((int64_t)g.L_k - 1) * a.vs_t * 2 + HD * 2);
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)k_extent, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)v_extent, kBufferFlags);
-  auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t stride_b, uint32_t thr, const Sub& s,
-                       lds_char* buf, bool is_v) {
-    const uint32_t soff = (uint32_t)(s.j * BK + s.h * SUB) * stride_b;
+  // K and V go straight to LDS through buffer resources, one per sub-tile: base =
+  // its first row, range = its real rows.  Lanes of rows past the end of a
+  // partial sub-tile fall outside the range and read zeros, and so do all lanes
+  // of the sub-tiles past the end of the list (range 0; their buffers are not
+  // read).  Every tile is then the same four loads, with no branch and no
+  // per-lane select, which also lets the compiler track exactly which LDS
+  // buffer each load writes (a direct-to-LDS global load would turn every LDS
+  // wait issued while it is in flight into lgkmcnt(0)).  Scores of rows past
+  // the end are masked to -inf, so their probabilities are exactly 0; V rows
+  // there hold zeros or an earlier tile's finite values.
+  uint32_t k_off[4], v_off[4];  // per load round: row offset + swizzled chunk
+  #pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    k_off[t] = t * 16u * ks_b + k_thr;
+    v_off[t] = t * 16u * vs_b + v_thr;
+  }
+  auto load_tile = [&](const char* base, uint32_t stride_b, const uint32_t (&off)[4], const Sub& s,
+                       lds_char* buf) {
+    const char* first = base + (size_t)(uint32_t)(s.j * BK + s.h * SUB) * stride_b;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(first), (short)0, (int)((uint32_t)s.len * stride_b), kBufferFlags);
     lds_char* const ldsb = buf + 4 * wave * (HD * 2);
-    if (s.len == SUB) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 16 * (HD * 2), 16, t * 16u * stride_b + thr, soff,
-                                                 0, 0);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 16 * t + st_row0;
-        const uint32_t src_off = r < s.len ? t * 16u * stride_b + thr
-                                           : (uint32_t)(((lane & 15) ^ (is_v ? 4 * (r & 3) : (r & 15))) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 16 * (HD * 2), 16, src_off, soff, 0, 0);
-      }
-    }
+  #pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 16 * (HD * 2), 16, off[t], 0, 0, 0);
   };
-  auto load_k = [&](const Sub& s, lds_char* buf) { load_tile(k_rsrc, ks_b, k_thr, s, buf, false); };
-  auto load_v = [&](const Sub& s, lds_char* buf) { load_tile(v_rsrc, vs_b, v_thr, s, buf, true); };
+  auto load_k = [&](const Sub& s, lds_char* buf) { load_tile(kbase, ks_b, k_off, s, buf); };
+  auto load_v = [&](const Sub& s, lds_char* buf) { load_tile(vbase, vs_b, v_off, s, buf); };
   auto k_frag = [&](lds_char* buf, int kt, int ks) -> bf16x8 {
     typedef const __attribute__((address_space(3))) bf16x8* lds_bf16x8;
     return *(lds_bf16x8)(buf + kt * 32 * (HD * 2) + k_row + (((2 * ks) ^ k_sw) << 4));
@@ -304,12 +298,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
 
   // Prologue: sub-tiles c0 (K and V), c1 (K) in flight; S of c0.  The reference
   // max starts at the max of c0.
+  // The V buffers start as zeros, so the rows past the end of a partial tile
+  // (which the loads leave alone) always hold finite values.
+  {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i* lds_v4i;
+    const int t = tid;
+  #pragma unroll
+    for (int i = 0; i < kTile / 16 / 256; ++i) {
+      *(lds_v4i)(vb[0] + (i * 256 + t) * 16) = v4i{0, 0, 0, 0};
+      *(lds_v4i)(vb[1] + (i * 256 + t) * 16) = v4i{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
   Sub cur = make_sub(next_valid(beg), 0);
   Sub nxt = advance(cur);
   if (cur.p < end) {
     load_k(cur, kb[0]);
     load_v(cur, vb[0]);
-    if (nxt.p < end) load_k(nxt, kb[1]);
+    load_k(nxt, kb[1]);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -361,8 +368,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     f32x16(&s_cur)[SUB / 32] = PAR == 0 ? sA : sB;
     f32x16(&s_nxt)[SUB / 32] = PAR == 0 ? sB : sA;
     const Sub nn = advance(nxt);
-    if (nn.p < end) load_k(nn, k_cur);
-    if (nxt.p < end) load_v(nxt, v_nxt);
+    load_k(nn, k_cur);
+    load_v(nxt, v_nxt);
     const float mc = m_run * c;
 
     // Phase 1.  MFMA i: key tile i & 1, feature step i >> 1.  P values 2i, 2i + 1
