@@ -184,10 +184,10 @@ def main():
             if events is not None:
                 events[n][0].record(stream)
             if args.dense:
-                S.dense_attn_fwd(s["Q"], s["K"], s["V"], s["sc"], out=s["out"])
                 if events is not None:
                     events[n][1].record(stream)
                     events[n][2].record(stream)
+                S.dense_attn_fwd(s["Q"], s["K"], s["V"], s["sc"], out=s["out"])
             else:
                 S.sparstar_pool_score(s["Q"], s["K"], s["sc"], s["qp"], s["kp"], s["scores"])
                 if events is not None:
