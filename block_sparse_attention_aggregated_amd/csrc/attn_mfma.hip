@@ -1,4 +1,4 @@
-// K3/K4: block-sparse (and dense) attention forward on gfx950 bf16 MFMA.
+// Block-sparse (and dense) attention forward on gfx950 bf16 MFMA.
 //
 // "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis",
 // section 5 "Forward-Only Sparse Execution" and "Complexity and Scope": each
@@ -184,11 +184,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     return make_sub(next_valid(s.p + 1), 0);
   };
 
-  // K and V staging (direct to LDS): wavefront w, round t (0..3) fills rows
+  // K and V staging (direct to LDS): wavefront w, load pass t (0..3) fills rows
   // 16t + 4w .. +4 of a sub-tile; lane i writes row +i/16 at physical chunk i%16.
   // K rows hold logical chunk c at physical chunk c ^ (row & 15); V rows at
   // c ^ 4(row & 3), which moves whole 64-byte groups (the 32-feature slices).
-  const int st_row0 = 4 * wave + (lane >> 4);  // row in round 0; round t adds 16t
+  const int st_row0 = 4 * wave + (lane >> 4);  // row in pass 0; pass t adds 16t
   // In-head byte offsets fit in 32 bits (the host routes larger layouts elsewhere).
   const uint32_t ks_b = (uint32_t)a.ks_t * 2u, vs_b = (uint32_t)a.vs_t * 2u;  // bytes per key
   const uint32_t k_thr = (uint32_t)st_row0 * ks_b + (uint32_t)(((lane & 15) ^ (st_row0 & 15)) * 16);
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   // wait issued while it is in flight into lgkmcnt(0)).  Scores of rows past
   // the end are masked to -inf, so their probabilities are exactly 0; V rows
   // there hold zeros or an earlier tile's finite values.
-  uint32_t k_off[4], v_off[4];  // per load round: row offset + swizzled chunk
+  uint32_t k_off[4], v_off[4];  // per load pass: row offset + swizzled chunk
   #pragma unroll
   for (int t = 0; t < 4; ++t) {
     k_off[t] = t * 16u * ks_b + k_thr;

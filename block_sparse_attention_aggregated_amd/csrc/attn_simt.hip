@@ -1,4 +1,4 @@
-// K3/K4, float32 path: block-sparse (and dense) attention forward for float32
+// Float32 path: block-sparse (and dense) attention forward for float32
 // inputs and for the shapes the MFMA kernel does not cover (head_dim 64,
 // 64-token blocks).  Same semantics as the MFMA kernel ("SparSTAR: Sparse
 // Attention for SpaceTime AutoRegressive Video Synthesis", section 5

@@ -1,4 +1,4 @@
-// K1: block mean-pooling and aggregated-QK block scores.
+// Block mean-pooling and aggregated-QK block scores.
 //
 // "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis",
 // section 5 "Original-order block partition": contiguous blocks of b tokens,

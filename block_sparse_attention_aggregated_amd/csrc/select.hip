@@ -1,4 +1,4 @@
-// K2: clip-aware per-row top-k block selection, written as CSR.
+// Clip-aware per-row top-k block selection, written as CSR.
 //
 // "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis",
 // section 5 "Clip-Dependent Retained and Selectable Blocks" and appendix A.7
