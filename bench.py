@@ -48,8 +48,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p",
-                    help="720p (default), 480p, 192p, tiny_f32, sweep, or a 720p_sweep_sN scale")
-    ap.add_argument("--density", type=float, default=None, help="default: 0.2 at 720p, else the workload's")
+                    help="720p (default), 480p, 192p, tiny_f32, sweep (four 720p-video scales of a later "
+                         "clip), clip1 (the same scales of a first clip under the decreasing schedule), or "
+                         "one scale by name")
+    ap.add_argument("--density", type=float, default=None,
+                    help="default: 0.2 at 720p and sweep, each scale's own density otherwise")
     ap.add_argument("--out-dtype", choices=("bf16", "f32"), default=None)
     ap.add_argument("--dense", action="store_true", help="time dense_attn_fwd (density 1 baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -63,8 +66,8 @@ def parse():
 
 def workload_configs(name):
     from block_sparse_attention_aggregated_amd import inputs as I
-    if name == "sweep":
-        return list(I.SWEEP)
+    if name in I.SEQUENCES:
+        return list(I.SEQUENCES[name])
     return [I.WORKLOADS[name]]
 
 
@@ -102,7 +105,7 @@ def traffic_record():
     return rec if rec.get("kernel_sha256") == src else None
 
 
-def cpu_baseline(cfg, density, Q, K, V, rows_per_head):
+def cpu_baseline(cfg, density, policy, Q, K, V, rows_per_head):
     """Time the float64 oracle on a bounded sample of the scale: pooling, scoring and
     selection of every head, and attention of rows_per_head query blocks per head
     (first, last and seeded random ones); the attention time is extrapolated to all
@@ -125,7 +128,7 @@ def cpu_baseline(cfg, density, Q, K, V, rows_per_head):
             k = K[bi, h].cpu().double().numpy()
             v = V[bi, h].cpu().double().numpy()
             t0 = time.perf_counter()
-            res = O.scale_head(q, k, v, cfg.len_text, cfg.len_ref, b, sigma, density, rows=[])
+            res = O.scale_head(q, k, v, cfg.len_text, cfg.len_ref, b, sigma, density, policy, rows=[])
             t_sel += time.perf_counter() - t0
             pick = rng.choice(nq, max(0, min(nq, rows_per_head) - 2), replace=False).tolist()
             rows = sorted({0, nq - 1, *pick})[:max(rows_per_head, 1)]
@@ -161,18 +164,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfgs = workload_configs(args.workload)
-    density = args.density if args.density is not None else (0.2 if args.workload in ("720p", "sweep")
-                                                            else cfgs[0].densities[0])
+    fixed = args.density if args.density is not None else (0.2 if args.workload in ("720p", "sweep") else None)
     print(f"# generating {args.workload} inputs", file=sys.stderr, flush=True)
     scales = []
     for cfg in cfgs:
         Q, K, V = I.make_inputs(cfg, device=dev)
         od = {"bf16": torch.bfloat16, "f32": torch.float32, None: Q.dtype}[args.out_dtype]
         sc = S.Scale(cfg.len_text, cfg.len_ref, cfg.block, cfg.softmax_scale)
+        density = fixed if fixed is not None else cfg.densities[0]
         qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
-        rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, density)
+        rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, density, cfg.policy)
         out = torch.empty(Q.shape, dtype=od, device=dev)
-        scales.append(dict(cfg=cfg, Q=Q, K=K, V=V, sc=sc, qp=qp, kp=kp, scores=scores, rp=rp, ci=ci, out=out))
+        scales.append(dict(cfg=cfg, Q=Q, K=K, V=V, sc=sc, qp=qp, kp=kp, scores=scores, rp=rp, ci=ci, out=out,
+                           density=density, policy=cfg.policy))
     torch.cuda.synchronize()
     for s in scales:
         s["flops"] = (4 * s["cfg"].head_dim * s["cfg"].batch * s["cfg"].heads * s["cfg"].len_q * s["cfg"].len_k
@@ -192,8 +196,8 @@ def main():
                 S.sparstar_pool_score(s["Q"], s["K"], s["sc"], s["qp"], s["kp"], s["scores"])
                 if events is not None:
                     events[n][1].record(stream)
-                S.sparstar_select_blocks(s["scores"], s["Q"], s["K"], s["sc"], density, row_ptr=s["rp"],
-                                         col_idx=s["ci"])
+                S.sparstar_select_blocks(s["scores"], s["Q"], s["K"], s["sc"], s["density"], s["policy"],
+                                         row_ptr=s["rp"], col_idx=s["ci"])
                 if events is not None:
                     events[n][2].record(stream)
                 S.sparstar_bsa_fwd(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"])
@@ -220,7 +224,8 @@ def main():
         tot = np.array([e[n][0].elapsed_time(e[n][3]) for e in ev])
         cfg = s["cfg"]
         per_scale.append({
-            "scale": cfg.name, "len_q": cfg.len_q, "len_k": cfg.len_k,
+            "scale": cfg.name, "len_q": cfg.len_q, "len_k": cfg.len_k, "density": s["density"],
+            "policy": "first clip" if s["policy"] == 1 else "later clip",
             "ms_pool_score": float(pool.mean()), "ms_select": float(sel.mean()),
             "ms_attention": float(att.mean()), "ms_attention_median": float(np.median(att)),
             "ms_scale": float(tot.mean()),
@@ -252,7 +257,8 @@ def main():
         "config": {
             "workload": ("720p final scale: 72,000 queries, keys 512 text + 72,000 preceding-clip + "
                          "72,000 current" if args.workload == "720p" else args.workload),
-            "heads": cfg0.heads, "head_dim": cfg0.head_dim, "block": cfg0.block, "density": density,
+            "heads": cfg0.heads, "head_dim": cfg0.head_dim, "block": cfg0.block,
+            "density": scales[0]["density"] if len(scales) == 1 else [s["density"] for s in scales],
             "mode": "dense" if args.dense else "sparse",
             "out_dtype": str(scales[0]["out"].dtype).replace("torch.", ""),
             "parallelism": "single GPU",
@@ -265,7 +271,8 @@ def main():
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": (traffic["bytes_per_launch"] if traffic and traffic.get("workload") == args.workload
-                        and abs(traffic.get("density", -1) - density) < 1e-12 and not args.dense else None),
+                        and len(scales) == 1 and abs(traffic.get("density", -1) - scales[0]["density"]) < 1e-12
+                        and not args.dense else None),
         },
     }
     if not args.dense and len(scales) == 1:
@@ -285,7 +292,8 @@ def main():
     if not args.no_cpu_baseline and not args.dense:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         s = scales[-1]
-        rec["cpu_baseline"] = cpu_baseline(s["cfg"], density, s["Q"], s["K"], s["V"], args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(s["cfg"], s["density"], s["policy"], s["Q"], s["K"], s["V"],
+                                           args.cpu_rows)
         print(f"# oracle sample: {rec['cpu_baseline']['sample']}", file=sys.stderr, flush=True)
     line = json.dumps(rec)
     print(line, flush=True)

@@ -67,6 +67,7 @@ class ScaleConfig:
     n_sinks: int = 2
     sink_gain: float = 4.0
     pos_amplitude: float = 1.0
+    policy: int = 0                   # 0: later clip (text kept), 1: first clip (text + ref kept)
 
     @property
     def len_q(self) -> int:
@@ -108,7 +109,47 @@ SWEEP = tuple(
                 seed=DEFAULT_SEED + i)
     for i, g in enumerate(SWEEP_GRIDS))
 
-WORKLOADS = {c.name: c for c in (TINY, S192P, S480P, S720P) + SWEEP}
+# First clip of a 720p video under the pages' decreasing schedule: the four
+# sparsified scales keep the text and the final image-pyramid scale
+# (1 x 45 x 80 = 3,600 tokens, here in the reference segment) dense and rank the
+# current-scale blocks at densities 0.625, 0.1875, 0.1875, 0.09375 (SparSTAR
+# full text, section 5 "Clip-Dependent Retained and Selectable Blocks";
+# appendix A.7).  The image tokens take the reference coordinates of the
+# recipe below (one frame, shifted by one clip).
+CLIP1_DENSITIES = (0.625, 0.1875, 0.1875, 0.09375)
+CLIP1 = tuple(
+    ScaleConfig(f"720p_clip1_s{i}", heads=32, head_dim=128, block=128, grid=g,
+                ref_grid=(1, 45, 80), len_text=512, densities=(d,), dtype="bf16",
+                seed=DEFAULT_SEED + 10 + i, policy=1)
+    for i, (g, d) in enumerate(zip(SWEEP_GRIDS, CLIP1_DENSITIES)))
+
+# Second clip of a ten-second 720p video: the same four scales as SWEEP (same
+# inputs), the preceding clip's final scale ranked jointly with the current
+# scale, at the same decreasing schedule (appendix A.7).
+CLIP2 = tuple(c.with_(name=f"720p_clip2_s{i}", densities=(d,))
+              for i, (c, d) in enumerate(zip(SWEEP, CLIP1_DENSITIES)))
+
+# 480p: the five-second setting sparsifies the four finest scales of its one
+# clip, the ten-second setting those of its second clip, whose keys hold the
+# first clip's final scale (appendix A.6).  The pages' scale grids are not in
+# the text; the four grids below scale the final 30 x 52 grid by the 720p
+# sweep's side ratios (about 1/2, 2/3, 5/6, 1).  32 heads as in the 8B backbone
+# (appendix A.5).
+GRIDS_480P = ((20, 15, 26), (20, 20, 35), (20, 25, 44), (20, 30, 52))
+CLIP1_480P = tuple(
+    ScaleConfig(f"480p_clip1_s{i}", heads=32, head_dim=128, block=128, grid=g,
+                ref_grid=(1, 30, 52), len_text=512, densities=(d,), dtype="bf16",
+                seed=DEFAULT_SEED + 20 + i, policy=1)
+    for i, (g, d) in enumerate(zip(GRIDS_480P, CLIP1_DENSITIES)))
+CLIP2_480P = tuple(
+    ScaleConfig(f"480p_clip2_s{i}", heads=32, head_dim=128, block=128, grid=g,
+                ref_grid=(20, 30, 52), len_text=512, densities=(d,), dtype="bf16",
+                seed=DEFAULT_SEED + 30 + i)
+    for i, (g, d) in enumerate(zip(GRIDS_480P, CLIP1_DENSITIES)))
+
+WORKLOADS = {c.name: c for c in (TINY, S192P, S480P, S720P) + SWEEP + CLIP1 + CLIP2 + CLIP1_480P + CLIP2_480P}
+SEQUENCES = {"sweep": SWEEP, "clip1": CLIP1, "clip2": CLIP2, "clip1_480p": CLIP1_480P,
+             "clip2_480p": CLIP2_480P}
 
 
 def grid_coords(grid: Sequence[int], t_shift: float) -> np.ndarray:

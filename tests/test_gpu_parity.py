@@ -388,6 +388,45 @@ def test_strided_views():
     assert torch.equal(outp, ref)
 
 
+# ---------------------------------------------------------------- clip policies and the schedule
+
+@pytest.mark.parametrize("name,heads", [("720p_clip1_s0", 2), ("720p_clip1_s3", 2), ("720p_clip1_s1", None),
+                                        ("480p_clip1_s3", 2), ("480p_clip2_s0", 2), ("480p_clip2_s3", 4)])
+def test_clip_schedule_end_to_end(name, heads):
+    """A sparsified scale of a first or later clip at its density in the decreasing
+    schedule.  First clip: text and image blocks retained, the current scale ranked;
+    later clip: text retained, preceding clip and current scale ranked jointly.
+    Selection on every row of the checked heads, attention on sampled query blocks,
+    against the oracle under the same policy."""
+    cfg = I.WORKLOADS[name] if heads is None else I.WORKLOADS[name].with_(heads=heads)
+    rho = cfg.densities[0]
+    print_case("clip schedule", cfg.name, cfg.heads, rho, cfg.policy)
+    Q, K, V = inputs(cfg)
+    (out, lse), (sc, rp, ci) = S.scale_forward(Q, K, V, scale_of(cfg), rho, policy=cfg.policy,
+                                               return_lse=True)
+    torch.cuda.synchronize()
+    lists = csr_rows(rp, ci)
+    b = cfg.block
+    nq = O.num_blocks(cfg.len_q, b)
+    R, C = O.retained_and_candidates(cfg.len_text, cfg.len_ref, cfg.len_q, b, cfg.policy)
+    kk = O.budget(len(C), rho)
+    assert len(R) == S.num_retained(S.problem(Q, K, V, scale_of(cfg)), cfg.policy)
+    check_heads = range(cfg.heads) if heads is not None else [0, cfg.heads - 1]
+    swaps = 0
+    for h in check_heads:
+        S_ref = O.block_scores(O.pool_blocks(head_np(Q, h), b), O.pool_blocks(head_np(K, h), b),
+                               cfg.softmax_scale)
+        ref_sets = O.select_blocks(S_ref, R, C, kk)
+        for i in range(nq):
+            swaps += compare_row_selection(lists[h * nq + i], ref_sets[i], S_ref[i], len(R), kk)
+    print(f"retained {len(R)} candidates {len(C)} budget {kk}; near-tie swaps {swaps}")
+
+    def sampler(h):
+        rng = np.random.default_rng(200 + h)
+        return sorted({0, nq - 1, *rng.choice(nq, 4, replace=False).tolist()})
+    _check_attention(cfg, Q, K, V, lists, out, lse, list(check_heads), sampler, True)
+
+
 # ---------------------------------------------------------------- full size (sampled)
 
 @pytest.mark.slow

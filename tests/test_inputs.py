@@ -100,3 +100,23 @@ def test_locality_makes_near_blocks_score_higher():
         j = (i + 17) % (cfg.len_q // b)
         off.append(qb @ k[r1 + j * b:r1 + (j + 1) * b].mean(0))
     assert np.mean(diag) > np.mean(off) + 1.0
+
+
+def test_clip_schedules_follow_the_pages():
+    """First- and later-clip workloads: the four sparsified scales at the pages'
+    decreasing density schedule (tests/golden/pages_figures.json, appendix A.6/A.7)."""
+    import json
+    import os
+    figs = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")))
+    sched = next(f["value"] for f in figs["figures"] if f["name"] == "density_schedule")
+    for clip, policy, ref_len, grids, final in (
+            (I.CLIP1, 1, 3600, I.SWEEP_GRIDS, 72000), (I.CLIP2, 0, 72000, I.SWEEP_GRIDS, 72000),
+            (I.CLIP1_480P, 1, 1560, I.GRIDS_480P, 31200), (I.CLIP2_480P, 0, 31200, I.GRIDS_480P, 31200)):
+        assert [c.densities[0] for c in clip] == sched
+        assert [c.policy for c in clip] == [policy] * 4
+        assert [c.grid for c in clip] == list(grids)
+        assert [c.len_ref for c in clip] == [ref_len] * 4
+        assert clip[-1].len_q == final and all(c.heads == 32 for c in clip)
+        assert [c.len_q for c in clip] == sorted(c.len_q for c in clip)
+    # the later clip reuses the sweep's inputs
+    assert [c.seed for c in I.CLIP2] == [c.seed for c in I.SWEEP]
