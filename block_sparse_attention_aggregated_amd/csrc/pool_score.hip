@@ -10,8 +10,8 @@
 // tokens x D features (32 KB for bf16, b = D = 128) with 16-byte loads, each
 // 16-lane group covering one 256-byte token row, and reduces the rows in
 // float32 through cross-lane shuffles and a small LDS exchange.
-// score_kernel is a small float32 GEMM per (batch, head): 64 x 64 output
-// tiles, K = D, operands staged through LDS, 4 x 4 outputs per thread.
+// score_kernel is a small float32 GEMM per (batch, head) on the float32
+// matrix cores: 64 x 128 output tiles, K = D.
 
 #include "sparstar_internal.h"
 
@@ -103,67 +103,115 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolScoreArgs a) {
   }
 }
 
-// S[bh, i, j] = sigma * sum_d qp[bh, i, d] * kp[bh, j, d].  Tile 64 x 64, 256 threads,
-// 4 x 4 outputs per thread; the D dimension is staged in chunks of 32 through LDS.
-constexpr int kTile = 64, kDc = 32;
+// S[bh, i, j] = sigma * sum_d qp[bh, i, d] * kp[bh, j, d] on the float32 matrix
+// cores (v_mfma_f32_32x32x2_f32, float32 products and sums).  A workgroup of 4
+// wavefronts computes a 64 x 128 tile (query blocks x key blocks); wavefront w
+// the 32 x 64 part (w >> 1, w & 1) as two MFMA tiles of 32 x 32.  The 64 pooled
+// query rows and 128 key rows go through LDS 32 features at a time: coalesced
+// 128-byte row segments into registers (the next chunk's loads are in flight
+// while the current chunk is multiplied), then into row-padded LDS tiles.  For
+// MFMA step s of a chunk, lane l supplies feature 16 (l >> 5) + s of row l & 31
+// of each of its tiles (the summation order within the 2-wide MFMA step is
+// free, as long as both operands use the same one), read from LDS 4 features at
+// a time.
+// Workgroups are placed XCD-aware: XCD x (= id mod 8) scores the heads
+// bh = x, x + 8, ..., so a head's pooled rows stay in one XCD's L2.
+// Output: register r of a lane holds row 8 (r >> 2) + 4 (l >> 5) + (r & 3) and
+// column l & 31 of its 32 x 32 tile.
+constexpr int kTileI = 64, kTileJ = 128;
+constexpr int kXcds = 8;
+constexpr int kDc = 32;           // features per chunk
+constexpr int kPad = kDc + 4;     // LDS row pitch in floats (144 B: conflict-free 16-byte reads)
 
 template <int D>
-__global__ __launch_bounds__(256) void score_kernel(PoolScoreArgs a, int tiles_i, int tiles_j) {
-  __shared__ float As[kDc][kTile + 4];
-  __shared__ float Bs[kDc][kTile + 4];
+__global__ __launch_bounds__(256, 2) void score_kernel(PoolScoreArgs a, int tiles_i, int tiles_j) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kChunks = D / kDc;
+  __shared__ __attribute__((aligned(16))) float As[kTileI][kPad];
+  __shared__ __attribute__((aligned(16))) float Bs[kTileJ][kPad];
   const Geometry& g = a.g;
-  const int64_t tile = blockIdx.x;
   const int64_t per_bh = (int64_t)tiles_i * tiles_j;
-  const int64_t bh = tile / per_bh;
-  const int rem = (int)(tile - bh * per_bh);
-  const int ti = rem / tiles_j, tj = rem - (rem / tiles_j) * tiles_j;
-  const int i0 = ti * kTile, j0 = tj * kTile;
+  const int64_t k = blockIdx.x / kXcds;
+  const int64_t bh = (k / per_bh) * kXcds + blockIdx.x % kXcds;
+  if (bh >= (int64_t)g.B * g.H) return;  // uniform over the workgroup
+  const int rem = (int)(k % per_bh);
+  const int ti = rem / tiles_j, tj = rem - ti * tiles_j;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r32 = lane & 31, hl = lane >> 5;
   const float* qp = a.q_pool + bh * g.n_q * D;
   const float* kp = a.k_pool + bh * g.n_k * D;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
 
-  float acc[4][4];
+  // Staging: thread t moves query rows (t >> 3) + 32 m, m = 0, 1, and key rows
+  // (t >> 3) + 32 m, m = 0..3, 16 bytes at feature 4 (t & 7).  Rows past the end
+  // copy the last row: they only feed outputs that are not stored.
+  constexpr int kMa = kTileI / 32, kMb = kTileJ / 32;
+  const int sr = tid >> 3, sc = 4 * (tid & 7);
+  const float* ga[kMa];
+  const float* gb[kMb];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int m = 0; m < kMa; ++m) ga[m] = qp + (int64_t)min(ti * kTileI + sr + 32 * m, g.n_q - 1) * D + sc;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc[r][s] = 0.f;
+  for (int m = 0; m < kMb; ++m) gb[m] = kp + (int64_t)min(tj * kTileJ + sr + 32 * m, g.n_k - 1) * D + sc;
+  f32x4 ra[kMa], rb[kMb];
+  auto gload = [&](int c) {
+#pragma unroll
+    for (int m = 0; m < kMa; ++m) ra[m] = *reinterpret_cast<const f32x4*>(ga[m] + c * kDc);
+#pragma unroll
+    for (int m = 0; m < kMb; ++m) rb[m] = *reinterpret_cast<const f32x4*>(gb[m] + c * kDc);
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int m = 0; m < kMa; ++m) *reinterpret_cast<f32x4*>(&As[sr + 32 * m][sc]) = ra[m];
+#pragma unroll
+    for (int m = 0; m < kMb; ++m) *reinterpret_cast<f32x4*>(&Bs[sr + 32 * m][sc]) = rb[m];
+  };
 
-  // Loader: 64 rows x 32 columns per operand = 512 float4; 2 per thread per operand.
-  for (int d0 = 0; d0 < D; d0 += kDc) {
+  f32x16 acc[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = threadIdx.x + u * 256;
-      const int row = idx / (kDc / 4), col4 = idx % (kDc / 4);
-      float4 qa = make_float4(0.f, 0.f, 0.f, 0.f), kb = qa;
-      if (i0 + row < g.n_q) qa = *reinterpret_cast<const float4*>(qp + (int64_t)(i0 + row) * D + d0 + col4 * 4);
-      if (j0 + row < g.n_k) kb = *reinterpret_cast<const float4*>(kp + (int64_t)(j0 + row) * D + d0 + col4 * 4);
-      As[col4 * 4 + 0][row] = qa.x; As[col4 * 4 + 1][row] = qa.y;
-      As[col4 * 4 + 2][row] = qa.z; As[col4 * 4 + 3][row] = qa.w;
-      Bs[col4 * 4 + 0][row] = kb.x; Bs[col4 * 4 + 1][row] = kb.y;
-      Bs[col4 * 4 + 2][row] = kb.z; Bs[col4 * 4 + 3][row] = kb.w;
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+
+  const int arow = (wave >> 1) * 32 + r32, brow = (wave & 1) * 64 + r32;
+  gload(0);
+  lstore();
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    if (c + 1 < kChunks) gload(c + 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // features 16 hl + 4q .. +4
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&As[arow][16 * hl + 4 * q]);
+      f32x4 bv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) bv[u] = *reinterpret_cast<const f32x4*>(&Bs[brow + 32 * u][16 * hl + 4 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[u][e], acc[u], 0, 0, 0);
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int d = 0; d < kDc; ++d) {
-      const float4 x = *reinterpret_cast<const float4*>(&As[d][ty * 4]);
-      const float4 y = *reinterpret_cast<const float4*>(&Bs[d][tx * 4]);
-      const float xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[r][s] = fmaf(xa[r], ya[s], acc[r][s]);
+    if (c + 1 < kChunks) {
+      __syncthreads();
+      lstore();
+      __syncthreads();
     }
-    __syncthreads();
   }
+
+  const int i0 = ti * kTileI + (wave >> 1) * 32 + 4 * hl, j0 = tj * kTileJ + (wave & 1) * 64 + r32;
   float* S = a.scores + bh * (int64_t)g.n_q * g.n_k;
+  const bool interior = (ti + 1) * kTileI <= g.n_q && (tj + 1) * kTileJ <= g.n_k;  // uniform
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = i0 + ty * 4 + r;
-    if (i >= g.n_q) continue;
+  for (int u = 0; u < 2; ++u) {
+    const int j = j0 + 32 * u;
+    float* col = S + (int64_t)i0 * g.n_k + j;
+    if (interior) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int j = j0 + tx * 4 + s;
-      if (j < g.n_k) S[(int64_t)i * g.n_k + j] = a.sigma * acc[r][s];
+      for (int r = 0; r < 16; ++r) col[(8 * (r >> 2) + (r & 3)) * g.n_k] = a.sigma * acc[u][r];
+    } else if (j < g.n_k) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (i0 + 8 * (r >> 2) + (r & 3) < g.n_q) col[(8 * (r >> 2) + (r & 3)) * g.n_k] = a.sigma * acc[u][r];
     }
   }
 }
@@ -185,8 +233,10 @@ hipError_t launch_pool_score(const PoolScoreArgs& a, hipStream_t s) {
   else
     e = a.g.D == 128 ? launch_pool<float, 128>(a, s) : launch_pool<float, 64>(a, s);
   if (e != hipSuccess) return e;
-  const int ti = (a.g.n_q + kTile - 1) / kTile, tj = (a.g.n_k + kTile - 1) / kTile;
-  const int64_t tiles = (int64_t)a.g.B * a.g.H * ti * tj;
+  const int ti = (a.g.n_q + kTileI - 1) / kTileI, tj = (a.g.n_k + kTileJ - 1) / kTileJ;
+  // XCD-aware grid: ceil(B*H / 8) head groups of 8, one per XCD lane of the id.
+  const int64_t tiles = ((int64_t)a.g.B * a.g.H + kXcds - 1) / kXcds * kXcds * ti * tj;
+  if (tiles > 0xffffffffll) return hipErrorInvalidValue;
   if (tiles > 0) {
     if (a.g.D == 128)
       hipLaunchKernelGGL(score_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, s, a, ti, tj);
