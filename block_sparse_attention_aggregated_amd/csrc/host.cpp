@@ -359,4 +359,109 @@ sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const v
   });
 }
 
+sparstar_status sparstar_block_mass(const sparstar_problem* p, const void* q, const void* k, const float* lse,
+                                    float* mass, void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar_status s = check_problem_impl(p);
+    if (s != SPARSTAR_OK) return s;
+    if (!q || !k || !lse || !mass) return fail(SPARSTAR_ERR_NULL, "q, k, lse and mass must be non-NULL");
+    if (!is_aligned16(q) || !is_aligned16(k) || (reinterpret_cast<uintptr_t>(lse) & 3u) ||
+        (reinterpret_cast<uintptr_t>(mass) & 3u))
+      return fail(SPARSTAR_ERR_LAYOUT, "q and k must be 16-byte aligned, lse and mass 4-byte aligned");
+    sparstar::MassArgs a;
+    a.g = geometry(p);
+    if ((int64_t)a.g.B * a.g.H * a.g.n_q == 0 || a.g.n_k == 0) return ok();
+    a.dtype = p->dtype;
+    a.q = q;
+    a.k = k;
+    a.qs_b = p->q_stride[0]; a.qs_h = p->q_stride[1]; a.qs_t = p->q_stride[2];
+    a.ks_b = p->k_stride[0]; a.ks_h = p->k_stride[1]; a.ks_t = p->k_stride[2];
+    a.lse = lse;
+    a.mass = mass;
+    a.sigma = p->softmax_scale;
+    a.small_extent = (a.g.L_k + 128) * a.ks_t * 2 < ((int64_t)1 << 31);
+    if ((s = check_device()) != SPARSTAR_OK) return s;
+    return launched(sparstar::launch_block_mass(a, (hipStream_t)stream), "block_mass launch");
+  });
+}
+
+sparstar_status sparstar_selection_mass(const sparstar_problem* p, const float* mass, const int32_t* row_ptr,
+                                        const int32_t* col_idx, int64_t col_idx_len, float* row_mass,
+                                        void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar_status s = check_problem_impl(p);
+    if (s != SPARSTAR_OK) return s;
+    if (!mass || !row_ptr || !col_idx || !row_mass)
+      return fail(SPARSTAR_ERR_NULL, "mass, row_ptr, col_idx and row_mass must be non-NULL");
+    if (col_idx_len < 0) return fail(SPARSTAR_ERR_SHAPE, "col_idx_len must be >= 0");
+    if ((reinterpret_cast<uintptr_t>(mass) & 3u) || (reinterpret_cast<uintptr_t>(row_ptr) & 3u) ||
+        (reinterpret_cast<uintptr_t>(col_idx) & 3u) || (reinterpret_cast<uintptr_t>(row_mass) & 3u))
+      return fail(SPARSTAR_ERR_LAYOUT, "mass, row_ptr, col_idx and row_mass must be 4-byte aligned");
+    const sparstar::Geometry g = geometry(p);
+    sparstar::SelMassArgs a;
+    a.mass = mass;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.col_idx_len = col_idx_len;
+    a.rows = (int64_t)g.B * g.H * g.n_q;
+    a.n_q = g.n_q;
+    a.n_k = g.n_k;
+    a.b = g.b;
+    a.L_q = g.L_q;
+    a.out = row_mass;
+    if (a.rows == 0) return ok();
+    if ((s = check_device()) != SPARSTAR_OK) return s;
+    return launched(sparstar::launch_selection_mass(a, (hipStream_t)stream), "selection_mass launch");
+  });
+}
+
+sparstar_status sparstar_window_scores(const sparstar_problem* p, float* scores, void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar_status s = check_problem_impl(p);
+    if (s != SPARSTAR_OK) return s;
+    if (!scores) return fail(SPARSTAR_ERR_NULL, "scores must be non-NULL");
+    if (!is_aligned16(scores)) return fail(SPARSTAR_ERR_LAYOUT, "scores must be 16-byte aligned");
+    const sparstar::Geometry g = geometry(p);
+    const int64_t bh = (int64_t)g.B * g.H;
+    if (bh * g.n_q * g.n_k == 0) return ok();
+    if ((s = check_device()) != SPARSTAR_OK) return s;
+    return launched(sparstar::launch_window_scores(scores, bh, g.n_q, g.n_k, g.b, p->len_text + p->len_ref,
+                                                   (hipStream_t)stream),
+                    "window_scores launch");
+  });
+}
+
+sparstar_status sparstar_token_topk_mass(const sparstar_problem* p, const void* q, const void* k, const float* lse,
+                                         const int64_t* rows, int64_t n_rows, int64_t keep_tokens,
+                                         int64_t k_tokens, float* out, void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar_status s = check_problem_impl(p);
+    if (s != SPARSTAR_OK) return s;
+    if (n_rows < 0 || keep_tokens < 0 || k_tokens < 0)
+      return fail(SPARSTAR_ERR_SHAPE, "n_rows, keep_tokens and k_tokens must be >= 0");
+    if (n_rows == 0) return ok();
+    if (!q || !k || !lse || !rows || !out) return fail(SPARSTAR_ERR_NULL, "q, k, lse, rows and out must be non-NULL");
+    if (!is_aligned16(q) || !is_aligned16(k) || (reinterpret_cast<uintptr_t>(lse) & 3u) ||
+        (reinterpret_cast<uintptr_t>(rows) & 7u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+      return fail(SPARSTAR_ERR_LAYOUT, "q, k 16-byte, rows 8-byte, lse and out 4-byte aligned");
+    sparstar::TopkArgs a;
+    a.g = geometry(p);
+    if ((int64_t)a.g.B * a.g.H * a.g.L_q == 0) return fail(SPARSTAR_ERR_SHAPE, "no queries to list");
+    a.dtype = p->dtype;
+    a.q = q;
+    a.k = k;
+    a.qs_b = p->q_stride[0]; a.qs_h = p->q_stride[1]; a.qs_t = p->q_stride[2];
+    a.ks_b = p->k_stride[0]; a.ks_h = p->k_stride[1]; a.ks_t = p->k_stride[2];
+    a.lse = lse;
+    a.rows = rows;
+    a.n_rows = n_rows;
+    a.keep_tokens = keep_tokens;
+    a.k_tokens = k_tokens;
+    a.sigma = p->softmax_scale;
+    a.out = out;
+    if ((s = check_device()) != SPARSTAR_OK) return s;
+    return launched(sparstar::launch_token_topk(a, (hipStream_t)stream), "token_topk_mass launch");
+  });
+}
+
 }  // extern "C"

@@ -56,7 +56,52 @@ struct AttnArgs {
   float sigma;
 };
 
+// Retained attention mass (dense softmax mass per block pair, of a selection,
+// and the token-wise Top-K bound).
+struct MassArgs {
+  Geometry g;
+  int dtype;
+  const void* q;
+  const void* k;
+  int64_t qs_b, qs_h, qs_t;
+  int64_t ks_b, ks_h, ks_t;
+  const float* lse;          // [B,H,L_q] packed, natural-log sum-exp of sigma*q.k over all keys
+  float* mass;               // [B,H,n_q,n_k]
+  float sigma;
+  bool small_extent;         // in-head byte offsets of K below 2^31 (MFMA path)
+};
+
+struct SelMassArgs {
+  const float* mass;         // [rows, n_k]
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t col_idx_len;
+  int64_t rows;              // B*H*n_q
+  int32_t n_q, n_k, b;
+  int64_t L_q;
+  float* out;                // [rows]
+};
+
+struct TopkArgs {
+  Geometry g;
+  int dtype;
+  const void* q;
+  const void* k;
+  int64_t qs_b, qs_h, qs_t;
+  int64_t ks_b, ks_h, ks_t;
+  const float* lse;          // [B,H,L_q] packed
+  const int64_t* rows;       // [n_rows]: query index bh*L_q + t
+  int64_t n_rows;
+  int64_t keep_tokens, k_tokens;
+  float sigma;
+  float* out;                // [n_rows]
+};
+
 hipError_t launch_pool_score(const PoolScoreArgs& a, hipStream_t s);
+hipError_t launch_block_mass(const MassArgs& a, hipStream_t s);
+hipError_t launch_selection_mass(const SelMassArgs& a, hipStream_t s);
+hipError_t launch_window_scores(float* out, int64_t bh, int n_q, int n_k, int b, int64_t offset, hipStream_t s);
+hipError_t launch_token_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // bf16 inputs, D = 128, b = 128 (MFMA path).
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);

@@ -63,6 +63,11 @@ _SIGS = {
     "sparstar_bsa_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
                                   _c_vp, _c_vp, _c_vp]),
     "dense_attn_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "sparstar_block_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "sparstar_selection_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]),
+    "sparstar_window_scores": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp]),
+    "sparstar_token_topk_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
+                                          _c_i64, _c_vp, _c_vp]),
 }
 
 
@@ -265,3 +270,62 @@ def scale_forward(q, k, v, scale: Scale, density: float, policy: int = POLICY_LA
     row_ptr, col_idx = sparstar_select_blocks(scores, q, k, scale, density, policy)
     res = sparstar_bsa_fwd(q, k, v, row_ptr, col_idx, scale, out_dtype=out_dtype, return_lse=return_lse)
     return res, (scores, row_ptr, col_idx)
+
+
+# ---------------------------------------------------------------- retained attention mass
+
+def sparstar_block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, scale: Scale,
+                        mass=None) -> torch.Tensor:
+    """Dense softmax mass per (query block, key block), float32 [B, H, n_q, n_k]."""
+    p = problem(q, k, None, scale)
+    B, H = q.shape[0], q.shape[1]
+    nq, nk = num_q_blocks(p), num_k_blocks(p)
+    if tuple(lse.shape) != tuple(q.shape[:3]) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise SparstarError(ERR_SHAPE, "lse must be contiguous float32 [B, H, L_q]")
+    if mass is None:
+        mass = torch.empty((B, H, nq, nk), dtype=torch.float32, device=q.device)
+    if tuple(mass.shape) != (B, H, nq, nk) or not mass.is_contiguous() or mass.dtype != torch.float32:
+        raise SparstarError(ERR_SHAPE, "mass must be contiguous float32 [B, H, n_q, n_k]")
+    _check(lib().sparstar_block_mass(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(lse), _ptr(mass),
+                                     _stream(q.device)))
+    return mass
+
+
+def sparstar_selection_mass(mass: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor,
+                            q: torch.Tensor, k: torch.Tensor, scale: Scale) -> torch.Tensor:
+    """Mean retained mass per query block of a CSR selection, float32 [B*H*n_q]."""
+    p = problem(q, k, None, scale)
+    rows = q.shape[0] * q.shape[1] * num_q_blocks(p)
+    if tuple(mass.shape) != (q.shape[0], q.shape[1], num_q_blocks(p), num_k_blocks(p)) or \
+            not mass.is_contiguous():
+        raise SparstarError(ERR_SHAPE, "mass must be contiguous [B, H, n_q, n_k]")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32 or row_ptr.numel() != rows + 1:
+        raise SparstarError(ERR_SHAPE, f"row_ptr must be int32 [{rows + 1}], col_idx int32")
+    out = torch.empty((rows,), dtype=torch.float32, device=mass.device)
+    _check(lib().sparstar_selection_mass(ctypes.byref(p), _ptr(mass), _ptr(row_ptr), _ptr(col_idx),
+                                         col_idx.numel(), _ptr(out), _stream(mass.device)))
+    return out
+
+
+def sparstar_window_scores(q: torch.Tensor, k: torch.Tensor, scale: Scale) -> torch.Tensor:
+    """Sliding-window scores, float32 [B, H, n_q, n_k] (minus the block-centre distance)."""
+    p = problem(q, k, None, scale)
+    out = torch.empty((q.shape[0], q.shape[1], num_q_blocks(p), num_k_blocks(p)), dtype=torch.float32,
+                      device=q.device)
+    _check(lib().sparstar_window_scores(ctypes.byref(p), _ptr(out), _stream(q.device)))
+    return out
+
+
+def sparstar_token_topk_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, rows: torch.Tensor,
+                             keep_tokens: int, k_tokens: int, scale: Scale) -> torch.Tensor:
+    """Token-wise Top-K mass of the listed queries (rows: int64 (b*H + h)*L_q + t), float32."""
+    p = problem(q, k, None, scale)
+    if rows.dtype != torch.int64 or not rows.is_contiguous():
+        raise SparstarError(ERR_SHAPE, "rows must be contiguous int64")
+    if tuple(lse.shape) != tuple(q.shape[:3]) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise SparstarError(ERR_SHAPE, "lse must be contiguous float32 [B, H, L_q]")
+    out = torch.empty((rows.numel(),), dtype=torch.float32, device=q.device)
+    _check(lib().sparstar_token_topk_mass(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(lse), _ptr(rows),
+                                          rows.numel(), int(keep_tokens), int(k_tokens), _ptr(out),
+                                          _stream(q.device)))
+    return out

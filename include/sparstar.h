@@ -165,6 +165,58 @@ sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const
 sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const void* k,
                                const void* v, void* out, float* lse, void* stream);
 
+/* ---------------- retained attention mass (the pages' quality measure of a selection) ---
+ * Section 4 "Analysis" (Figure 3; "Pattern Persistence across Clip Boundaries")
+ * and section 1 measure a selection by the share of each query's dense softmax
+ * mass it keeps, against the token-wise Top-K bound, the exact block oracle, a
+ * sliding window and random blocks.  With w_ts = exp(sigma*q_t.k_s - lse_t) the
+ * dense attention weight of query t on real key s (lse from dense_attn_fwd):
+ *   - the exact block oracle is sparstar_select_blocks fed the block mass below;
+ *   - a sliding window is sparstar_select_blocks fed sparstar_window_scores;
+ *   - random blocks are sparstar_select_blocks fed caller-drawn uniform numbers. */
+
+/* M[b, h, i, j] = sum over the real queries t of query block i and the real keys s of
+ * key block j of w_ts.  Row i sums to the number of real queries of block i.
+ *   q, k : inputs in p->dtype with p's strides (v and out strides are not used).
+ *   lse  : in, float32 [B, H, L_q] contiguous (dense_attn_fwd's lse output).
+ *   mass : out, float32 [B, H, n_q, n_k] contiguous.
+ * bf16 with D = 128 and b = 128 runs on bf16 MFMA (float32 exp2 and sums); other
+ * shapes on a float32 kernel.  Deterministic (fixed summation order). */
+sparstar_status sparstar_block_mass(const sparstar_problem* p, const void* q, const void* k,
+                                    const float* lse, float* mass, void* stream);
+
+/* Mean retained mass per query block of a block selection:
+ * row_mass[r] = sum over the entries j of row r (r = (b*H + h)*n_q + i) of mass[r, j],
+ * divided by the real queries of block i.  Entries outside [0, n_k) and positions
+ * outside [0, col_idx_len) are skipped; a block listed twice counts twice.
+ *   mass     : in, float32 [B, H, n_q, n_k] (sparstar_block_mass).
+ *   row_ptr  : in, int32 [B*H*n_q + 1];  col_idx: in, int32 [col_idx_len].
+ *   row_mass : out, float32 [B*H*n_q]. */
+sparstar_status sparstar_selection_mass(const sparstar_problem* p, const float* mass,
+                                        const int32_t* row_ptr, const int32_t* col_idx,
+                                        int64_t col_idx_len, float* row_mass, void* stream);
+
+/* Sliding-window scores: scores[b, h, i, j] = -|(j*b + b/2) - (L_text + L_ref + i*b + b/2)|,
+ * minus the distance in key-sequence position between the centres of key block j and
+ * query block i (query t is key L_text + L_ref + t).  Through sparstar_select_blocks
+ * every query block gets the k candidate blocks nearest to it, equal distances to the
+ * lower index.   scores: out, float32 [B, H, n_q, n_k] contiguous. */
+sparstar_status sparstar_window_scores(const sparstar_problem* p, float* scores, void* stream);
+
+/* Token-wise Top-K bound for listed queries: out[n] = sum of w_ts over the key tokens
+ * s < keep_tokens plus the k_tokens largest w_ts over the key tokens s >= keep_tokens
+ * (all of them if fewer), for query index rows[n] = (b*H + h)*L_q + t.  With
+ * keep_tokens = (retained blocks)*b and k_tokens = k*b this bounds the mass any
+ * selection of k candidate blocks keeps for that query.
+ *   q, k : inputs;  lse: in, float32 [B, H, L_q] (dense_attn_fwd).
+ *   rows : in, int64 [n_rows], 8-byte aligned; an index outside [0, B*H*L_q) gives NaN.
+ *   out  : out, float32 [n_rows].
+ * Weights in float32; the k-th largest is found exactly on their float32 values. */
+sparstar_status sparstar_token_topk_mass(const sparstar_problem* p, const void* q, const void* k,
+                                         const float* lse, const int64_t* rows, int64_t n_rows,
+                                         int64_t keep_tokens, int64_t k_tokens, float* out,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,9 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 13
+    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 17
+    assert {"sparstar_block_mass", "sparstar_selection_mass", "sparstar_window_scores",
+            "sparstar_token_topk_mass"} <= set(names)
     L = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -156,6 +158,29 @@ def test_null_and_alignment_and_density_and_capacity():
     assert st == S.ERR_CAPACITY and "capacity" in S.last_error()
     assert L.sparstar_select_blocks(ctypes.byref(p), b, 0.3, 0, None, b, nnz, None) == S.ERR_NULL
     assert S.status_string(S.ERR_CAPACITY) == "output capacity too small"
+
+
+@no_gpu
+def test_mass_entry_points_validate_before_any_device_call():
+    p = _prob(I.S192P)
+    L = S.lib()
+    b = ctypes.c_void_p(BOGUS)
+    odd = ctypes.c_void_p(BOGUS + 2)
+    assert L.sparstar_block_mass(None, b, b, b, b, None) == S.ERR_NULL
+    assert L.sparstar_block_mass(ctypes.byref(p), b, b, None, b, None) == S.ERR_NULL
+    assert L.sparstar_block_mass(ctypes.byref(p), odd, b, b, b, None) == S.ERR_LAYOUT
+    assert L.sparstar_selection_mass(ctypes.byref(p), b, b, None, 10, b, None) == S.ERR_NULL
+    assert L.sparstar_selection_mass(ctypes.byref(p), b, b, b, -1, b, None) == S.ERR_SHAPE
+    assert L.sparstar_selection_mass(ctypes.byref(p), odd, b, b, 10, b, None) == S.ERR_LAYOUT
+    assert L.sparstar_window_scores(ctypes.byref(p), None, None) == S.ERR_NULL
+    assert L.sparstar_window_scores(ctypes.byref(p), ctypes.c_void_p(BOGUS + 4), None) == S.ERR_LAYOUT
+    assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, b, -1, 0, 0, b, None) == S.ERR_SHAPE
+    assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, b, 4, -1, 0, b, None) == S.ERR_SHAPE
+    assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, None, 4, 0, 0, b, None) == S.ERR_NULL
+    assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, ctypes.c_void_p(BOGUS + 4), 4, 0, 0, b,
+                                      None) == S.ERR_LAYOUT
+    # nothing listed: nothing to do, no device needed
+    assert L.sparstar_token_topk_mass(ctypes.byref(p), None, None, None, None, 0, 0, 0, None, None) == S.OK
 
 
 @no_gpu
