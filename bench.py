@@ -16,8 +16,10 @@ inputs already resident in HBM.  Prints one JSON line:
   cpu_baseline the float64 CPU oracle on a bounded sample of the same scale,
                extrapolated to the whole scale (a baseline, not a target)
 
---dense times dense_attn_fwd instead (the density-1 baseline).  --gpus > 1
-is refused: this path runs on one GPU and shards by head with no exchange.
+--dense times dense_attn_fwd instead (the density-1 baseline); --mass measures
+the retained attention mass of the selection strategies and times the
+block-mass pass.  --gpus > 1 is refused: this path runs on one GPU and shards
+by head with no exchange.
 """
 
 from __future__ import annotations
@@ -60,6 +62,10 @@ def parse():
                     help="query blocks per head the oracle attends in its sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--mass", action="store_true",
+                    help="retained attention mass of the selection strategies instead (times block_mass)")
+    ap.add_argument("--mass-queries", type=int, default=512,
+                    help="sampled queries for the token-wise Top-K bound in --mass mode")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -150,12 +156,88 @@ def cpu_baseline(cfg, density, policy, Q, K, V, rows_per_head):
     }
 
 
+def run_mass(args):
+    """Retained attention mass of the block oracle, aggregated-QK (the method), a sliding window and
+    random blocks on one scale, plus the token-wise Top-K bound on sampled queries; times the block-mass
+    pass (QK^T over every key, exp2 and block sums) with HIP events on its stream."""
+    import torch
+
+    from block_sparse_attention_aggregated_amd import inputs as I
+    from block_sparse_attention_aggregated_amd import sparstar as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workload_configs(args.workload)[-1]
+    density = args.density if args.density is not None else (0.2 if args.workload == "720p" else cfg.densities[0])
+    sc = S.Scale(cfg.len_text, cfg.len_ref, cfg.block, cfg.softmax_scale)
+    print(f"# generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    Q, K, V = I.make_inputs(cfg, device=dev)
+    _, lse = S.dense_attn_fwd(Q, K, V, sc, return_lse=True)
+    mass = S.sparstar_block_mass(Q, K, lse, sc)
+    for _ in range(args.warmup):
+        S.sparstar_block_mass(Q, K, lse, sc, mass=mass)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    print(f"# timing {args.steps} block_mass launches", file=sys.stderr, flush=True)
+    for e0, e1 in ev:
+        e0.record(stream)
+        S.sparstar_block_mass(Q, K, lse, sc, mass=mass)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 2 * cfg.batch * cfg.heads * cfg.len_q * cfg.len_k * cfg.head_dim   # Q K^T over every key
+
+    # selections: block oracle (exact block mass), aggregated-QK, window, random
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    rnd = torch.rand(mass.shape, generator=gen, device=dev, dtype=torch.float32)
+    _, _, scores = S.sparstar_pool_score(Q, K, sc)
+    window = S.sparstar_window_scores(Q, K, sc)
+    res = {}
+    for name, src in (("block_oracle", mass), ("aggregated_qk", scores), ("window", window), ("random", rnd)):
+        rp, ci = S.sparstar_select_blocks(src, Q, K, sc, density, cfg.policy)
+        res[name] = float(S.sparstar_selection_mass(mass, rp, ci, Q, K, sc).mean())
+    p = S.problem(Q, K, None, sc)
+    r = S.num_retained(p, cfg.policy)
+    kk = S.blocks_per_row(p, density, cfg.policy) - r
+    g = torch.Generator(device=dev).manual_seed(99)
+    rows = torch.randint(0, cfg.batch * cfg.heads * cfg.len_q, (args.mass_queries,), generator=g, device=dev)
+    tok = S.sparstar_token_topk_mass(Q, K, lse, rows, r * cfg.block, kk * cfg.block, sc)
+    # the same queries under the block oracle's blocks, for the gap at matched queries
+    torch.cuda.synchronize()
+    res["token_topk_bound_sampled"] = float(tok.mean())
+    rec = {
+        "metric": "retained attention mass (mean over query blocks) and block-mass pass time",
+        "value": res["aggregated_qk"], "unit": "fraction of dense softmax mass", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "heads": cfg.heads, "density": density, "block": cfg.block,
+                   "policy": "first clip" if cfg.policy == 1 else "later clip",
+                   "token_bound_queries": args.mass_queries},
+        "retained_mass": res,
+        "gaps": {"blockization (token bound - block oracle)": res["token_topk_bound_sampled"] - res["block_oracle"],
+                 "scoring (block oracle - aggregated QK)": res["block_oracle"] - res["aggregated_qk"]},
+        "roofline": {"kernel": "sparstar_block_mass", "bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flop_per_launch": flops, "exp2_per_launch": cfg.batch * cfg.heads * cfg.len_q * cfg.len_k},
+    }
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by head with "
               "no exchange, so N GPUs would each run this same benchmark at H/N heads.", file=sys.stderr)
         sys.exit(2)
+    if args.mass:
+        run_mass(args)
+        return
     import torch
 
     from block_sparse_attention_aggregated_amd import inputs as I
