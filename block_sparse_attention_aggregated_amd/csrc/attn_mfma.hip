@@ -5,10 +5,11 @@
 // query block visits only the key blocks of its list, so the work scales with
 // the retained fraction of blocks; softmax over the real keys of those blocks.
 //
-// Shape: bf16 Q/K/V, head_dim 128, 128-token query and key blocks.
-// One workgroup (4 wavefronts) per query block, two workgroups per CU;
-// wavefront w owns queries 32w .. 32w+31 of the block.  Each 128-key block
-// is processed as two 64-key sub-tiles, double-buffered in LDS.  Per sub-tile:
+// Shape: bf16 Q/K/V, head_dim 128, query and key blocks of b = 64, 128 or 256
+// tokens.  One workgroup of b / 32 wavefronts per query block (two workgroups
+// per CU for b <= 128, one for b = 256); wavefront w owns queries 32w .. 32w+31
+// of the block.  Each key block is processed as b / 64 sub-tiles of 64 keys,
+// double-buffered in LDS.  Per sub-tile:
 //   S^T[key, query] = K Q^T   16 x v_mfma_f32_32x32x16_bf16 per wavefront in
 //                             two independent accumulator chains (A = K from
 //                             LDS, B = Q held in registers for the whole row),
@@ -65,10 +66,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BQ = 128;            // query block
-constexpr int BK = 128;            // key block
 constexpr int HD = 128;            // head_dim
-constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kBig = 18446744073709551616.0f;  // 2^64: bound on a lane's P sum per sub-tile
@@ -99,8 +97,23 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
-template <bool kDense, bool kOutBf16, bool kLse>
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int per_xcd) {
+// Block size kB (queries and keys): kB / 32 wavefronts, two workgroups per CU
+// (one at kB = 256, whose 8 wavefronts already fill the two slots of every SIMD).
+template <int kB>
+struct Shape {
+  static constexpr int BQ = kB, BK = kB;
+  static constexpr int kWaves = kB / 32;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kPerCu = kB == 256 ? 1 : 2;
+  static constexpr int kSubs = kB / 64;      // 64-key sub-tiles per key block
+  static constexpr int kPasses = 16 / kWaves;  // load passes of 4 rows per wavefront per sub-tile
+};
+
+template <int kB, bool kDense, bool kOutBf16, bool kLse>
+__global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_mfma_kernel(AttnArgs a, int per_xcd) {
+  constexpr int BQ = Shape<kB>::BQ, BK = Shape<kB>::BK;
+  constexpr int kThreads = Shape<kB>::kThreads, kWaves = Shape<kB>::kWaves;
+  constexpr int kSubs = Shape<kB>::kSubs, kPasses = Shape<kB>::kPasses;
   __shared__ __attribute__((aligned(16))) char k_lds0[kTile];
   __shared__ __attribute__((aligned(16))) char k_lds1[kTile];
   __shared__ __attribute__((aligned(16))) char v_lds0[kTile];
@@ -180,19 +193,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   };
   auto advance = [&](const Sub& s) -> Sub {
     if (s.p >= end) return s;
-    if (s.h == 0 && (int)g.L_k - s.j * BK > SUB) return make_sub(s.p, 1);
+    if constexpr (kSubs == 2) {
+      if (s.h == 0 && (int)g.L_k - s.j * BK > SUB) return make_sub(s.p, 1);
+    } else if constexpr (kSubs > 2) {
+      if (s.h + 1 < kSubs && (int)g.L_k - s.j * BK > (s.h + 1) * SUB) return make_sub(s.p, s.h + 1);
+    }
     return make_sub(next_valid(s.p + 1), 0);
   };
 
-  // K and V staging (direct to LDS): wavefront w, load pass t (0..3) fills rows
-  // 16t + 4w .. +4 of a sub-tile; lane i writes row +i/16 at physical chunk i%16.
-  // K rows hold logical chunk c at physical chunk c ^ (row & 15); V rows at
-  // c ^ 4(row & 3), which moves whole 64-byte groups (the 32-feature slices).
-  const int st_row0 = 4 * wave + (lane >> 4);  // row in pass 0; pass t adds 16t
+  // K and V staging (direct to LDS): wavefront w, load pass t (0 .. kPasses - 1)
+  // fills rows 4 kWaves t + 4w .. +4 of a sub-tile; lane i writes row + i/16 at
+  // physical chunk i%16.  K rows hold logical chunk c at physical chunk
+  // c ^ (row & 15); V rows at c ^ 4(row & 3), which moves whole 64-byte groups
+  // (the 32-feature slices).
+  const int st_row0 = 4 * wave + (lane >> 4);  // row in pass 0; pass t adds 4 kWaves t
   // In-head byte offsets fit in 32 bits (the host routes larger layouts elsewhere).
   const uint32_t ks_b = (uint32_t)a.ks_t * 2u, vs_b = (uint32_t)a.vs_t * 2u;  // bytes per key
-  const uint32_t k_thr = (uint32_t)st_row0 * ks_b + (uint32_t)(((lane & 15) ^ (st_row0 & 15)) * 16);
-  const uint32_t v_thr = (uint32_t)st_row0 * vs_b + (uint32_t)(((lane & 15) ^ (4 * (st_row0 & 3))) * 16);
 
   // LDS read offsets.  K: row kt*32 + l32, logical chunk 2ks + hl, physical chunk
   // (2ks + hl) ^ (row & 15) = 2ks ^ (hl ^ (l32 & 15)); kt adds 32 rows.
@@ -225,21 +241,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   // wait issued while it is in flight into lgkmcnt(0)).  Scores of rows past
   // the end are masked to -inf, so their probabilities are exactly 0; V rows
   // there hold zeros or an earlier tile's finite values.
-  uint32_t k_off[4], v_off[4];  // per load pass: row offset + swizzled chunk
+  uint32_t k_off[kPasses], v_off[kPasses];  // per load pass: row offset + swizzled chunk
   #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    k_off[t] = t * 16u * ks_b + k_thr;
-    v_off[t] = t * 16u * vs_b + v_thr;
+  for (int t = 0; t < kPasses; ++t) {
+    const int row = st_row0 + 4 * kWaves * t;
+    k_off[t] = (uint32_t)row * ks_b + (uint32_t)(((lane & 15) ^ (row & 15)) * 16);
+    v_off[t] = (uint32_t)row * vs_b + (uint32_t)(((lane & 15) ^ (4 * (row & 3))) * 16);
   }
-  auto load_tile = [&](const char* base, uint32_t stride_b, const uint32_t (&off)[4], const Sub& s,
+  auto load_tile = [&](const char* base, uint32_t stride_b, const uint32_t* off, const Sub& s,
                        lds_char* buf) {
     const char* first = base + (size_t)(uint32_t)(s.j * BK + s.h * SUB) * stride_b;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(first), (short)0, (int)((uint32_t)s.len * stride_b), kBufferFlags);
     lds_char* const ldsb = buf + 4 * wave * (HD * 2);
   #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 16 * (HD * 2), 16, off[t], 0, 0, 0);
+    for (int t = 0; t < kPasses; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 4 * kWaves * (HD * 2), 16, off[t], 0, 0, 0);
   };
   auto load_k = [&](const Sub& s, lds_char* buf) { load_tile(kbase, ks_b, k_off, s, buf); };
   auto load_v = [&](const Sub& s, lds_char* buf) { load_tile(vbase, vs_b, v_off, s, buf); };
@@ -305,9 +322,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
     typedef __attribute__((address_space(3))) v4i* lds_v4i;
     const int t = tid;
   #pragma unroll
-    for (int i = 0; i < kTile / 16 / 256; ++i) {
-      *(lds_v4i)(vb[0] + (i * 256 + t) * 16) = v4i{0, 0, 0, 0};
-      *(lds_v4i)(vb[1] + (i * 256 + t) * 16) = v4i{0, 0, 0, 0};
+    for (int i = 0; i < kTile / 16 / kThreads; ++i) {
+      *(lds_v4i)(vb[0] + (i * kThreads + t) * 16) = v4i{0, 0, 0, 0};
+      *(lds_v4i)(vb[1] + (i * kThreads + t) * 16) = v4i{0, 0, 0, 0};
     }
   }
   __syncthreads();
@@ -492,29 +509,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, int 
   }
 }
 
-template <bool kDense, bool kOutBf16, bool kLse>
+template <int kB, bool kDense, bool kOutBf16, bool kLse>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int per_xcd = (a.g.n_q + kXcds - 1) / kXcds;
   const int64_t grid = (int64_t)a.g.B * a.g.H * per_xcd * kXcds;
   if (grid > 0xffffffffll) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_mfma_kernel<kDense, kOutBf16, kLse>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                     per_xcd);
+  hipLaunchKernelGGL((attn_mfma_kernel<kB, kDense, kOutBf16, kLse>), dim3((unsigned)grid),
+                     dim3(Shape<kB>::kThreads), 0, s, a, per_xcd);
   return hipSuccess;
 }
 
-template <bool kDense, bool kOutBf16>
+template <int kB, bool kDense, bool kOutBf16>
 hipError_t launch2(const AttnArgs& a, hipStream_t s) {
-  return a.lse ? launch<kDense, kOutBf16, true>(a, s) : launch<kDense, kOutBf16, false>(a, s);
+  return a.lse ? launch<kB, kDense, kOutBf16, true>(a, s) : launch<kB, kDense, kOutBf16, false>(a, s);
+}
+
+template <int kB>
+hipError_t launch_b(const AttnArgs& a, hipStream_t s) {
+  const bool dense = a.row_ptr == nullptr;
+  const bool ob = a.out_dtype == 0;
+  return dense ? (ob ? launch2<kB, true, true>(a, s) : launch2<kB, true, false>(a, s))
+               : (ob ? launch2<kB, false, true>(a, s) : launch2<kB, false, false>(a, s));
 }
 
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-  if (a.g.D != HD || a.g.b != BQ || a.dtype != 0) return hipErrorInvalidValue;
-  const bool dense = a.row_ptr == nullptr;
-  const bool ob = a.out_dtype == 0;
-  const hipError_t e = dense ? (ob ? launch2<true, true>(a, s) : launch2<true, false>(a, s))
-                             : (ob ? launch2<false, true>(a, s) : launch2<false, false>(a, s));
+  if (a.g.D != HD || a.dtype != 0) return hipErrorInvalidValue;
+  hipError_t e;
+  switch (a.g.b) {
+    case 64: e = launch_b<64>(a, s); break;
+    case 128: e = launch_b<128>(a, s); break;
+    case 256: e = launch_b<256>(a, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return e != hipSuccess ? e : hipGetLastError();
 }
 

@@ -1,6 +1,5 @@
 // Float32 path: block-sparse (and dense) attention forward for float32
-// inputs and for the shapes the MFMA kernel does not cover (head_dim 64,
-// 64-token blocks).  Same semantics as the MFMA kernel ("SparSTAR: Sparse
+// inputs and for the shapes the MFMA kernel does not cover (head_dim 64).  Same semantics as the MFMA kernel ("SparSTAR: Sparse
 // Attention for SpaceTime AutoRegressive Video Synthesis", section 5
 // "Forward-Only Sparse Execution"): every query of block i attends, with a
 // softmax over real keys only, to the key blocks listed for row i.
@@ -24,7 +23,7 @@ template <>
 __device__ inline float to_f32<__bf16>(__bf16 x) { return (float)x; }
 
 template <typename T, int D, bool kDense, typename OutT>
-__global__ __launch_bounds__(128) void attn_simt_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
   __shared__ float Kc[kChunk][D + 1];
   __shared__ float Vc[kChunk][D + 1];
   const Geometry& g = a.g;
@@ -123,7 +122,7 @@ void launch2(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t s) {
-  if (a.g.b > 128) return hipErrorInvalidValue;
+  if (a.g.b > 256) return hipErrorInvalidValue;
   if (a.dtype == 0) a.g.D == 128 ? launch2<__bf16, 128>(a, s) : launch2<__bf16, 64>(a, s);
   else a.g.D == 128 ? launch2<float, 128>(a, s) : launch2<float, 64>(a, s);
   return hipGetLastError();

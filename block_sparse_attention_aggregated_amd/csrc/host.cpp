@@ -65,8 +65,8 @@ sparstar_status check_problem_impl(const sparstar_problem* p) {
     return fail(SPARSTAR_ERR_SHAPE, "len_q, len_text and len_ref must be >= 0");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(SPARSTAR_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", p->head_dim);
-  if (p->block != 64 && p->block != 128)
-    return fail(SPARSTAR_ERR_UNSUPPORTED, "block %d not built (64 or 128)", p->block);
+  if (p->block != 64 && p->block != 128 && p->block != 256)
+    return fail(SPARSTAR_ERR_UNSUPPORTED, "block %d not built (64, 128 or 256)", p->block);
   if ((p->dtype != SPARSTAR_BF16 && p->dtype != SPARSTAR_F32) ||
       (p->out_dtype != SPARSTAR_BF16 && p->out_dtype != SPARSTAR_F32))
     return fail(SPARSTAR_ERR_UNSUPPORTED, "dtype %d / out_dtype %d not built", p->dtype, p->out_dtype);
@@ -190,9 +190,9 @@ sparstar_status run_attn(const sparstar::AttnArgs& a, hipStream_t st) {
   sparstar_status s = check_device();
   if (s != SPARSTAR_OK) return s;
   // The MFMA kernel keeps in-head byte offsets in 32 bits.
-  const bool small_extent = (a.g.L_k + 128) * std::max(a.ks_t, a.vs_t) * 2 < ((int64_t)1 << 31) &&
-                            (a.g.L_q + 128) * std::max(a.qs_t, a.os_t) * 4 < ((int64_t)1 << 31);
-  const bool mfma = a.dtype == SPARSTAR_BF16 && a.g.D == 128 && a.g.b == 128 && small_extent;
+  const bool small_extent = (a.g.L_k + 256) * std::max(a.ks_t, a.vs_t) * 2 < ((int64_t)1 << 31) &&
+                            (a.g.L_q + 256) * std::max(a.qs_t, a.os_t) * 4 < ((int64_t)1 << 31);
+  const bool mfma = a.dtype == SPARSTAR_BF16 && a.g.D == 128 && small_extent;
   return launched(mfma ? sparstar::launch_attn_mfma(a, st) : sparstar::launch_attn_simt(a, st),
                   mfma ? "attention (bf16 MFMA) launch" : "attention (float32) launch");
 }
@@ -379,7 +379,7 @@ sparstar_status sparstar_block_mass(const sparstar_problem* p, const void* q, co
     a.lse = lse;
     a.mass = mass;
     a.sigma = p->softmax_scale;
-    a.small_extent = (a.g.L_k + 128) * a.ks_t * 2 < ((int64_t)1 << 31);
+    a.small_extent = (a.g.L_k + 256) * a.ks_t * 2 < ((int64_t)1 << 31);
     if ((s = check_device()) != SPARSTAR_OK) return s;
     return launched(sparstar::launch_block_mass(a, (hipStream_t)stream), "block_mass launch");
   });

@@ -178,13 +178,13 @@ __global__ __launch_bounds__(256, 2) void block_mass_mfma_kernel(MassArgs a, int
 
 // ---------------------------------------------------------------- SIMT block mass
 
-// One workgroup of b threads per (batch, head, query block), thread = query; keys
-// staged through LDS in float32, 32 at a time.
+// One workgroup of 256 threads per (batch, head, query block), thread = query (the
+// first b threads); keys staged through LDS in float32, 32 at a time.
 template <typename T, int D>
-__global__ __launch_bounds__(128) void block_mass_simt_kernel(MassArgs a) {
+__global__ __launch_bounds__(256) void block_mass_simt_kernel(MassArgs a) {
   constexpr int kChunk = 32;
   __shared__ float ks[kChunk][D + 1];
-  __shared__ float red[128];
+  __shared__ float red[256];
   const Geometry& g = a.g;
   const int64_t row = blockIdx.x;  // bh * n_q + i
   const int64_t bh = row / g.n_q;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(128) void block_mass_simt_kernel(MassArgs a) {
     // Fixed-order tree over the threads of the workgroup.
     red[tid] = valid ? sum : 0.f;
     __syncthreads();
-    for (int o = 64; o >= 1; o >>= 1) {
+    for (int o = 128; o >= 1; o >>= 1) {
       if (tid < o) red[tid] += red[tid + o];
       __syncthreads();
     }
@@ -415,7 +415,7 @@ hipError_t launch_block_mass(const MassArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(block_mass_mfma_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, per_xcd);
   } else {
     if (rows > 0xffffffffll) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)rows), block(128);
+    const dim3 grid((unsigned)rows), block(256);
     if (a.dtype == 0 && g.D == 128)
       hipLaunchKernelGGL((block_mass_simt_kernel<__bf16, 128>), grid, block, 0, s, a);
     else if (a.dtype == 0)

@@ -52,16 +52,16 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolScoreArgs a) {
   const int bi = (int)(bh / g.H), hi = (int)(bh - (int64_t)bi * g.H);
   const bool is_q = j < g.n_q;
   if (!is_q) j -= g.n_q;
-  const T* base;
+  const T* base_ptr;
   int64_t ts, L;
   float* dst;
   if (is_q) {
-    base = static_cast<const T*>(a.q) + bi * a.qs_b + hi * a.qs_h;
+    base_ptr = static_cast<const T*>(a.q) + bi * a.qs_b + hi * a.qs_h;
     ts = a.qs_t;
     L = g.L_q;
     dst = a.q_pool + (bh * g.n_q + j) * D;
   } else {
-    base = static_cast<const T*>(a.k) + bi * a.ks_b + hi * a.ks_h;
+    base_ptr = static_cast<const T*>(a.k) + bi * a.ks_b + hi * a.ks_h;
     ts = a.ks_t;
     L = g.L_k;
     dst = a.k_pool + (bh * g.n_k + j) * D;
@@ -74,23 +74,26 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolScoreArgs a) {
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-  // b / G rows per thread (8 for bf16 at b = D = 128); all loads issued first.
+  // 128 / G rows per thread and pass (8 for bf16 at D = 128), all loads of a pass
+  // issued first; blocks of 256 tokens take two passes.
   constexpr int kMaxRows = 128 / G > 0 ? 128 / G : 1;
-  float vals[kMaxRows][VEC];
+  for (int base = 0; base < n_tok; base += 128) {
+    float vals[kMaxRows][VEC];
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) {
-    const int t = grp + r * G;
-    if (t < n_tok) {
-      load16_to_f32(base + (t0 + t) * ts + c * VEC, vals[r]);
-    } else {
+    for (int r = 0; r < kMaxRows; ++r) {
+      const int t = base + grp + r * G;
+      if (t < n_tok) {
+        load16_to_f32(base_ptr + (t0 + t) * ts + c * VEC, vals[r]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) vals[r][e] = 0.f;
+        for (int e = 0; e < VEC; ++e) vals[r][e] = 0.f;
+      }
     }
+#pragma unroll
+    for (int r = 0; r < kMaxRows; ++r)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += vals[r][e];
   }
-#pragma unroll
-  for (int r = 0; r < kMaxRows; ++r)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] += vals[r][e];
 
 #pragma unroll
   for (int e = 0; e < VEC; ++e) red[grp][c * VEC + e] = acc[e];
@@ -227,7 +230,7 @@ hipError_t launch_pool(const PoolScoreArgs& a, hipStream_t s) {
 
 hipError_t launch_pool_score(const PoolScoreArgs& a, hipStream_t s) {
   hipError_t e;
-  if (a.g.b > 128) return hipErrorInvalidValue;  // pool_kernel holds up to 128 rows per workgroup
+  if (a.g.b > 256) return hipErrorInvalidValue;  // pool_kernel walks up to 256 rows per workgroup
   if (a.dtype == 0)
     e = a.g.D == 128 ? launch_pool<__bf16, 128>(a, s) : launch_pool<__bf16, 64>(a, s);
   else

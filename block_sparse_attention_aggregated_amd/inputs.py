@@ -147,7 +147,18 @@ CLIP2_480P = tuple(
                 seed=DEFAULT_SEED + 30 + i)
     for i, (g, d) in enumerate(zip(GRIDS_480P, CLIP1_DENSITIES)))
 
-WORKLOADS = {c.name: c for c in (TINY, S192P, S480P, S720P) + SWEEP + CLIP1 + CLIP2 + CLIP1_480P + CLIP2_480P}
+# Block-size ablation (appendix D.2 "Block-Size Ablation": 64 and 256 beside the
+# deployed 128): the 192p and tiny shapes for parity, the 720p final scale at
+# density 0.2 for timing.
+S192P_B64 = S192P.with_(name="192p_b64", block=64)
+S192P_B256 = S192P.with_(name="192p_b256", block=256)
+TINY_B256 = TINY.with_(name="tiny_f32_b256", block=256)
+S720P_B64 = S720P.with_(name="720p_b64", block=64, densities=(0.2,))
+S720P_B256 = S720P.with_(name="720p_b256", block=256, densities=(0.2,))
+BLOCK_SIZES = (S192P_B64, S192P_B256, TINY_B256, S720P_B64, S720P_B256)
+
+WORKLOADS = {c.name: c for c in (TINY, S192P, S480P, S720P) + SWEEP + CLIP1 + CLIP2 + CLIP1_480P + CLIP2_480P
+             + BLOCK_SIZES}
 SEQUENCES = {"sweep": SWEEP, "clip1": CLIP1, "clip2": CLIP2, "clip1_480p": CLIP1_480P,
              "clip2_480p": CLIP2_480P}
 

@@ -71,7 +71,8 @@ typedef struct {
   int32_t batch;          /* B >= 0                                                     */
   int32_t heads;          /* H >= 0                                                     */
   int32_t head_dim;       /* D: 64 or 128                                               */
-  int32_t block;          /* b: 64 or 128, the same for query and key blocks            */
+  int32_t block;          /* b: 64, 128 or 256, the same for query and key blocks
+                             (128 deployed; 64 and 256 from appendix D.2)                */
   int64_t len_q;          /* L_q >= 0: current-scale tokens (queries, last keys)        */
   int64_t len_text;       /* L_text >= 0                                                */
   int64_t len_ref;        /* L_ref >= 0: the preceding clip's final scale               */
@@ -153,8 +154,9 @@ sparstar_status sparstar_select_blocks(const sparstar_problem* p, const float* s
  *   row_ptr  : in, int32 [B*H*n_q + 1];  col_idx: in, int32 [col_idx_len].
  *   out      : out, p->out_dtype with p->o_stride; rows >= L_q are not written.
  *   lse      : out, nullable, float32 [B, H, L_q] contiguous: sigma*max + log(sum exp).
- * bf16 inputs with D = 128 and b = 128 run on bf16 MFMA with float32 softmax and
- * accumulation; other shapes and float32 inputs run a float32 kernel. */
+ * bf16 inputs with D = 128 run on bf16 MFMA with float32 softmax and accumulation
+ * for every block size (64, 128, 256: the block sizes of appendix D.2 "Block-Size
+ * Ablation"); D = 64 and float32 inputs run a float32 kernel. */
 sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const void* k,
                                  const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                                  int64_t col_idx_len, void* out, float* lse, void* stream);

@@ -103,6 +103,7 @@ def _status(fn, *args):
 @pytest.mark.parametrize("mutate,code", [
     (lambda p: setattr(p, "head_dim", 96), S.ERR_UNSUPPORTED),
     (lambda p: setattr(p, "block", 32), S.ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "block", 512), S.ERR_UNSUPPORTED),
     (lambda p: setattr(p, "dtype", 7), S.ERR_UNSUPPORTED),
     (lambda p: setattr(p, "out_dtype", -1), S.ERR_UNSUPPORTED),
     (lambda p: setattr(p, "batch", -1), S.ERR_SHAPE),

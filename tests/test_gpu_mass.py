@@ -49,7 +49,8 @@ def _oracle_mass_row(q, k, i, cfg):
 
 
 @pytest.mark.parametrize("cfg,heads,rows", [(I.TINY, None, None), (I.S192P, [0, 15], None),
-                                            (I.S480P, [7], [0, 1, 100, 243])])
+                                            (I.S480P, [7], [0, 1, 100, 243]), (I.S192P_B256, [3], None),
+                                            (I.S192P_B64, [5], [0, 1, 40, 78])])
 def test_block_mass_parity(cfg, heads, rows):
     print_case("block_mass", cfg.name)
     Q, K, V = I.make_inputs(cfg, device=DEV)

@@ -427,6 +427,55 @@ def test_clip_schedule_end_to_end(name, heads):
     _check_attention(cfg, Q, K, V, lists, out, lse, list(check_heads), sampler, True)
 
 
+# ---------------------------------------------------------------- block sizes 64 and 256
+
+@pytest.mark.parametrize("name,heads,nsample", [("192p_b64", [0, 15], 12), ("192p_b256", [0, 15], None),
+                                                ("tiny_f32_b256", None, None)])
+def test_block_sizes_end_to_end(name, heads, nsample):
+    """Block sizes of the pages' ablation beside the deployed 128: pooled scores, selection
+    (near-tie rule) and attention against the oracle, and the dense path equal to a full
+    block list bit for bit (bf16: the MFMA kernel at 2 and 8 wavefronts per workgroup)."""
+    cfg = I.WORKLOADS[name]
+    rho = cfg.densities[0]
+    print_case("block size", cfg.name, cfg.block, rho)
+    Q, K, V = inputs(cfg)
+    sc = scale_of(cfg)
+    bf16_in = cfg.dtype == "bf16"
+    qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, rho)
+    out, lse = S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    b = cfg.block
+    nq, nk = O.num_blocks(cfg.len_q, b), O.num_blocks(cfg.len_k, b)
+    R, C = O.retained_and_candidates(cfg.len_text, cfg.len_ref, cfg.len_q, b)
+    kk = O.budget(len(C), rho)
+    lists = csr_rows(rp, ci)
+    check_heads = range(cfg.heads) if heads is None else heads
+    for h in check_heads:
+        q, k = head_np(Q, h), head_np(K, h)
+        qbar, kbar = O.pool_blocks(q, b), O.pool_blocks(k, b)
+        S_ref = O.block_scores(qbar, kbar, cfg.softmax_scale)
+        assert np.max(np.abs(to_f64(qp[0, h]) - qbar)) < 2e-6 * max(1.0, np.abs(qbar).max())
+        bound = cfg.head_dim * 6e-8 * cfg.softmax_scale * (np.abs(qbar) @ np.abs(kbar).T) + 1e-7
+        assert np.all(np.abs(to_f64(scores[0, h]) - S_ref) <= bound)
+        ref_sets = O.select_blocks(S_ref, R, C, kk)
+        for i in range(nq):
+            compare_row_selection(lists[h * nq + i], ref_sets[i], S_ref[i], len(R), kk)
+    sampler = None
+    if nsample:
+        def sampler(h):
+            rng = np.random.default_rng(300 + h)
+            return sorted({0, nq - 1, *rng.choice(nq, nsample, replace=False).tolist()})
+    _check_attention(cfg, Q, K, V, lists, out, lse, list(check_heads), sampler, bf16_in)
+    # the dense path is the sparse path over every block
+    full_rp = torch.arange(0, (cfg.heads * nq + 1) * nk, nk, dtype=torch.int32, device=DEV)
+    full_ci = torch.arange(nk, dtype=torch.int32, device=DEV).repeat(cfg.heads * nq)
+    a = S.sparstar_bsa_fwd(Q, K, V, full_rp, full_ci, sc)
+    d = S.dense_attn_fwd(Q, K, V, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(a, d)
+
+
 # ---------------------------------------------------------------- full size (sampled)
 
 @pytest.mark.slow
