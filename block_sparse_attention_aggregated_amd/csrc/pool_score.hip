@@ -20,8 +20,8 @@ namespace {
 
 constexpr int kPoolThreads = 256;
 
-__device__ inline void load16_to_f32(const __bf16* src, float* dst8) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(src);
+// 16 loaded bytes as float32: eight bf16 (the high halves of float32) or four float32.
+__device__ inline void to_f32x(uint4 raw, float* dst8, __bf16) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -30,9 +30,11 @@ __device__ inline void load16_to_f32(const __bf16* src, float* dst8) {
   }
 }
 
-__device__ inline void load16_to_f32(const float* src, float* dst4) {
-  const float4 raw = *reinterpret_cast<const float4*>(src);
-  dst4[0] = raw.x; dst4[1] = raw.y; dst4[2] = raw.z; dst4[3] = raw.w;
+__device__ inline void to_f32x(uint4 raw, float* dst4, float) {
+  dst4[0] = __uint_as_float(raw.x);
+  dst4[1] = __uint_as_float(raw.y);
+  dst4[2] = __uint_as_float(raw.z);
+  dst4[3] = __uint_as_float(raw.w);
 }
 
 // One workgroup per (batch, head, block), query blocks first then key blocks.
@@ -74,25 +76,26 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolScoreArgs a) {
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-  // 128 / G rows per thread and pass (8 for bf16 at D = 128), all loads of a pass
-  // issued first; blocks of 256 tokens take two passes.
+  // 128 / G rows per thread and pass (8 for bf16 at D = 128); blocks of 256 tokens
+  // take two passes.  All loads of a pass are issued before any is used: every
+  // lane loads a real row (rows past the end re-read the last real row) and the
+  // rows past the end are then zeroed by a select, so no load sits in a branch.
   constexpr int kMaxRows = 128 / G > 0 ? 128 / G : 1;
   for (int base = 0; base < n_tok; base += 128) {
-    float vals[kMaxRows][VEC];
+    uint4 raw[kMaxRows];
 #pragma unroll
     for (int r = 0; r < kMaxRows; ++r) {
-      const int t = base + grp + r * G;
-      if (t < n_tok) {
-        load16_to_f32(base_ptr + (t0 + t) * ts + c * VEC, vals[r]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) vals[r][e] = 0.f;
-      }
+      const int t = min(base + grp + r * G, n_tok - 1);
+      raw[r] = *reinterpret_cast<const uint4*>(base_ptr + (t0 + t) * ts + c * VEC);
     }
 #pragma unroll
-    for (int r = 0; r < kMaxRows; ++r)
+    for (int r = 0; r < kMaxRows; ++r) {
+      float v[VEC];
+      to_f32x(raw[r], v, T{});
+      const bool ok = base + grp + r * G < n_tok;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += vals[r][e];
+      for (int e = 0; e < VEC; ++e) acc[e] += ok ? v[e] : 0.f;
+    }
   }
 
 #pragma unroll
