@@ -62,6 +62,15 @@ def parse():
                     help="query blocks per head the oracle attends in its sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--uneven", action="store_true",
+                    help="time bsa_fwd over seeded random block lists of uneven length (same mean as the "
+                         "density) instead of the selection's uniform ones; the selector is not run")
+    ap.add_argument("--random-even", action="store_true",
+                    help="with --uneven: random lists of the selection's length for every row (the control)")
+    ap.add_argument("--balanced", action="store_true",
+                    help="run the attention through sparstar_bsa_fwd_balanced (rows started longest list first)")
+    ap.add_argument("--longest-first", action="store_true",
+                    help="with --uneven: give the longest lists to the rows the kernel dispatches first")
     ap.add_argument("--mass", action="store_true",
                     help="retained attention mass of the selection strategies instead (times block_mass)")
     ap.add_argument("--mass-queries", type=int, default=512,
@@ -229,6 +238,44 @@ def run_mass(args):
             f.write(line + "\n")
 
 
+def dispatch_order(B, H, n_q, xcds=8):
+    """Rows in the order bsa_fwd's workgroups are numbered: workgroup w = 8 m + x runs query block
+    x * ceil(n_q/8) + m % ceil(n_q/8) of head m // ceil(n_q/8) (a workgroup past n_q exits)."""
+    per = -(-n_q // xcds)
+    order = []
+    for w in range(B * H * per * xcds):
+        m, x = divmod(w, xcds)
+        bh, qi = divmod(m, per)
+        qi += x * per
+        if qi < n_q:
+            order.append(bh * n_q + qi)
+    return np.array(order)
+
+
+def uneven_lists(n_rows, n_k, r, k, seed=7, even=False, first=None):
+    """Seeded block lists (row_ptr, col_idx as numpy int32) whose candidate counts are uniform on
+    [1, 2k - 1] (mean k), or all k if `even`: the retained prefix [0, r) plus that many distinct
+    random candidates of [r, n_k), ascending.  An input recipe for timing, not a selection."""
+    rng = np.random.default_rng(seed)
+    n_c = n_k - r
+    counts = rng.integers(1, min(2 * k - 1, n_c) + 1, size=n_rows)
+    if even:
+        counts[:] = k
+    if first is not None:          # longest lists to the rows dispatched first
+        srt = np.sort(counts)[::-1]
+        counts = np.empty_like(srt)
+        counts[first] = srt
+    keys = rng.random((n_rows, n_c), dtype=np.float32)
+    rank = np.argsort(keys, axis=1)
+    rows = []
+    for i in range(n_rows):
+        pick = np.sort(rank[i, :counts[i]]) + r
+        rows.append(np.concatenate([np.arange(r), pick]))
+    row_ptr = np.zeros(n_rows + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum([len(x) for x in rows])
+    return row_ptr.astype(np.int32), np.concatenate(rows).astype(np.int32), counts
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,9 +303,21 @@ def main():
         density = fixed if fixed is not None else cfg.densities[0]
         qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
         rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, density, cfg.policy)
+        if args.uneven:
+            p = S.problem(Q, K, None, sc)
+            r = S.num_retained(p, cfg.policy)
+            k = S.blocks_per_row(p, density, cfg.policy) - r
+            n_rows = cfg.batch * cfg.heads * S.num_q_blocks(p)
+            print(f"# drawing uneven block lists for {n_rows} rows", file=sys.stderr, flush=True)
+            first = dispatch_order(cfg.batch, cfg.heads, S.num_q_blocks(p)) if args.longest_first else None
+            rp_np, ci_np, counts = uneven_lists(n_rows, S.num_k_blocks(p), r, k, even=args.random_even, first=first)
+            rp, ci = torch.from_numpy(rp_np).to(dev), torch.from_numpy(ci_np).to(dev)
+            print(f"# candidates per row: min {counts.min()} mean {counts.mean():.1f} max {counts.max()} "
+                  f"(uniform selection: {k})", file=sys.stderr, flush=True)
         out = torch.empty(Q.shape, dtype=od, device=dev)
+        ws = torch.empty((S.balance_workspace_bytes(S.problem(Q, K, None, sc)) // 4,), dtype=torch.int32, device=dev)
         scales.append(dict(cfg=cfg, Q=Q, K=K, V=V, sc=sc, qp=qp, kp=kp, scores=scores, rp=rp, ci=ci, out=out,
-                           density=density, policy=cfg.policy))
+                           density=density, policy=cfg.policy, ws=ws))
     torch.cuda.synchronize()
     for s in scales:
         s["flops"] = (4 * s["cfg"].head_dim * s["cfg"].batch * s["cfg"].heads * s["cfg"].len_q * s["cfg"].len_k
@@ -278,11 +337,16 @@ def main():
                 S.sparstar_pool_score(s["Q"], s["K"], s["sc"], s["qp"], s["kp"], s["scores"])
                 if events is not None:
                     events[n][1].record(stream)
-                S.sparstar_select_blocks(s["scores"], s["Q"], s["K"], s["sc"], s["density"], s["policy"],
-                                         row_ptr=s["rp"], col_idx=s["ci"])
+                if not args.uneven:
+                    S.sparstar_select_blocks(s["scores"], s["Q"], s["K"], s["sc"], s["density"], s["policy"],
+                                             row_ptr=s["rp"], col_idx=s["ci"])
                 if events is not None:
                     events[n][2].record(stream)
-                S.sparstar_bsa_fwd(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"])
+                if args.balanced:
+                    S.sparstar_bsa_fwd_balanced(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"],
+                                                workspace=s["ws"])
+                else:
+                    S.sparstar_bsa_fwd(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"])
             if events is not None:
                 events[n][3].record(stream)
 
@@ -341,7 +405,9 @@ def main():
                          "72,000 current" if args.workload == "720p" else args.workload),
             "heads": cfg0.heads, "head_dim": cfg0.head_dim, "block": cfg0.block,
             "density": scales[0]["density"] if len(scales) == 1 else [s["density"] for s in scales],
-            "mode": "dense" if args.dense else "sparse",
+            "mode": ("dense" if args.dense else (("sparse, random lists of equal length" if args.random_even else
+                                                  "sparse, uneven random lists") if args.uneven else "sparse"))
+                    + (", balanced (longest list first)" if args.balanced else ""),
             "out_dtype": str(scales[0]["out"].dtype).replace("torch.", ""),
             "parallelism": "single GPU",
         },
@@ -354,7 +420,7 @@ def main():
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": (traffic["bytes_per_launch"] if traffic and traffic.get("workload") == args.workload
                         and len(scales) == 1 and abs(traffic.get("density", -1) - scales[0]["density"]) < 1e-12
-                        and not args.dense else None),
+                        and not args.dense and not args.uneven else None),
         },
     }
     if not args.dense and len(scales) == 1:
@@ -371,7 +437,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         rec["calib_copy_bytes"] = 2 * n * 4
-    if not args.no_cpu_baseline and not args.dense:
+    if not args.no_cpu_baseline and not args.dense and not args.uneven:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         s = scales[-1]
         rec["cpu_baseline"] = cpu_baseline(s["cfg"], s["density"], s["policy"], s["Q"], s["K"], s["V"],

@@ -45,7 +45,8 @@
 // conflicts without padding.  One barrier per sub-tile.  The block lists are
 // read through the scalar cache.
 //
-// Workgroups are mapped to rows XCD-aware.  Consecutive workgroup ids are
+// Workgroups are mapped to rows XCD-aware (with a row order for uneven lists,
+// each XCD starts the rows of its segment of a head longest list first).  Consecutive workgroup ids are
 // dispatched round-robin over the 8 XCDs; XCD x takes query blocks
 // [x * per_xcd, (x + 1) * per_xcd) of each head, per_xcd = ceil(n_q / 8), and
 // all XCDs go through the heads in the same order.  The workgroups resident on
@@ -124,10 +125,13 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
   const Geometry& g = a.g;
   // Workgroup id -> (head, query block): XCD x = id % 8 takes query blocks
   // [x * per_xcd, (x + 1) * per_xcd) of every head, heads in order.
+  // With a row order (uneven lists), the m-th workgroup of segment (head, XCD) runs the
+  // segment's m-th longest row instead of its m-th.
   const int64_t k = blockIdx.x / kXcds;
   const int64_t bh = k / per_xcd;
-  const int qi = (int)(blockIdx.x % kXcds) * per_xcd + (int)(k - bh * per_xcd);
-  if (qi >= g.n_q) return;  // uniform over the workgroup
+  const int xcd = (int)(blockIdx.x % kXcds), m = (int)(k - bh * per_xcd);
+  const int qi = a.row_order ? a.row_order[(bh * kXcds + xcd) * per_xcd + m] : xcd * per_xcd + m;
+  if (qi < 0 || qi >= g.n_q) return;  // uniform over the workgroup
   const int64_t row = bh * g.n_q + qi;
   const int bi = (int)(bh / g.H), hi = (int)(bh - (int64_t)bi * g.H);
   const int tid = threadIdx.x, lane = tid & 63;

@@ -181,6 +181,7 @@ sparstar_status attn_common(const sparstar_problem* p, const void* q, const void
   a.vs_b = p->v_stride[0]; a.vs_h = p->v_stride[1]; a.vs_t = p->v_stride[2];
   a.os_b = p->o_stride[0]; a.os_h = p->o_stride[1]; a.os_t = p->o_stride[2];
   a.sigma = p->softmax_scale;
+  a.row_order = nullptr;
   return SPARSTAR_OK;
 }
 
@@ -461,6 +462,47 @@ sparstar_status sparstar_token_topk_mass(const sparstar_problem* p, const void* 
     a.out = out;
     if ((s = check_device()) != SPARSTAR_OK) return s;
     return launched(sparstar::launch_token_topk(a, (hipStream_t)stream), "token_topk_mass launch");
+  });
+}
+
+int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p) {
+  if (check_problem_impl(p) != SPARSTAR_OK) return -1;
+  return sparstar::row_order_entries((int64_t)p->batch * p->heads, (int32_t)ceil_div(p->len_q, p->block)) *
+         (int64_t)sizeof(int32_t);
+}
+
+sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void* q, const void* k, const void* v,
+                                          const int32_t* row_ptr, const int32_t* col_idx, int64_t col_idx_len,
+                                          void* out, float* lse, void* workspace, int64_t workspace_bytes,
+                                          void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar::AttnArgs a;
+    sparstar_status s = attn_common(p, q, k, v, out, a);
+    if (s != SPARSTAR_OK) return s;
+    if (!row_ptr || !col_idx || !workspace)
+      return fail(SPARSTAR_ERR_NULL, "row_ptr, col_idx and workspace must be non-NULL");
+    if (col_idx_len < 0) return fail(SPARSTAR_ERR_SHAPE, "col_idx_len must be >= 0");
+    if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+      return fail(SPARSTAR_ERR_LAYOUT, "row_ptr, col_idx, lse and workspace must be 4-byte aligned");
+    const int64_t rows = (int64_t)a.g.B * a.g.H * a.g.n_q;
+    const int64_t need = sparstar::row_order_entries((int64_t)a.g.B * a.g.H, a.g.n_q) * (int64_t)sizeof(int32_t);
+    if (workspace_bytes < need)
+      return fail(SPARSTAR_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                  (long long)need);
+    a.lse = lse;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.col_idx_len = col_idx_len;
+    if (rows == 0) return ok();
+    if ((s = check_device()) != SPARSTAR_OK) return s;
+    int32_t* order = static_cast<int32_t*>(workspace);
+    s = launched(sparstar::launch_row_order(row_ptr, (int64_t)a.g.B * a.g.H, a.g.n_q, col_idx_len, order,
+                                            (hipStream_t)stream),
+                 "row order launch");
+    if (s != SPARSTAR_OK) return s;
+    a.row_order = order;
+    return run_attn(a, (hipStream_t)stream);
   });
 }
 

@@ -54,6 +54,7 @@ struct AttnArgs {
   const int32_t* col_idx;
   int64_t col_idx_len;
   float sigma;
+  const int32_t* row_order;  // nullable: per (head, XCD) segment, the query blocks longest list first
 };
 
 // Retained attention mass (dense softmax mass per block pair, of a selection,
@@ -103,6 +104,11 @@ hipError_t launch_selection_mass(const SelMassArgs& a, hipStream_t s);
 hipError_t launch_window_scores(float* out, int64_t bh, int n_q, int n_k, int b, int64_t offset, hipStream_t s);
 hipError_t launch_token_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// Query blocks of each (head, XCD) segment ordered by list length, longest first:
+// order[(bh * 8 + x) * ceil(n_q / 8) + m], -1 past a segment's end.
+int64_t row_order_entries(int64_t bh, int32_t n_q);
+hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int64_t col_idx_len, int32_t* order,
+                            hipStream_t s);
 // bf16 inputs, D = 128, b = 128 (MFMA path).
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 // Any supported shape/dtype (float32 path).

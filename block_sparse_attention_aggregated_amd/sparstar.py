@@ -63,6 +63,9 @@ _SIGS = {
     "sparstar_bsa_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
                                   _c_vp, _c_vp, _c_vp]),
     "dense_attn_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "sparstar_balance_workspace_bytes": (_c_i64, [ctypes.POINTER(Problem)]),
+    "sparstar_bsa_fwd_balanced": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
+                                           _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "sparstar_block_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "sparstar_selection_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]),
     "sparstar_window_scores": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp]),
@@ -180,6 +183,10 @@ def select_nnz(p: Problem, density: float, policy: int = POLICY_LATER_CLIP) -> i
     return lib().sparstar_select_nnz(ctypes.byref(p), density, policy)
 
 
+def balance_workspace_bytes(p: Problem) -> int:
+    return lib().sparstar_balance_workspace_bytes(ctypes.byref(p))
+
+
 def status_string(s: int) -> str:
     return lib().sparstar_status_string(s).decode()
 
@@ -248,6 +255,28 @@ def sparstar_bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr:
         raise SparstarError(ERR_SHAPE, f"row_ptr must hold {rows + 1} entries, contiguous")
     _check(lib().sparstar_bsa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
                                   col_idx.numel(), _ptr(out), _ptr(lse), _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def sparstar_bsa_fwd_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                              col_idx: torch.Tensor, scale: Scale, out=None, out_dtype=None,
+                              return_lse: bool = False, workspace=None):
+    """sparstar_bsa_fwd with the rows started longest list first (uneven lists)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    p = problem(q, k, v, scale, out=out)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise SparstarError(ERR_UNSUPPORTED, "row_ptr and col_idx must be int32")
+    rows = q.shape[0] * q.shape[1] * num_q_blocks(p)
+    if row_ptr.numel() != rows + 1 or not row_ptr.is_contiguous() or not col_idx.is_contiguous():
+        raise SparstarError(ERR_SHAPE, f"row_ptr must hold {rows + 1} entries, contiguous")
+    need = balance_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) // 4,), dtype=torch.int32, device=q.device)
+    _check(lib().sparstar_bsa_fwd_balanced(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                           _ptr(col_idx), col_idx.numel(), _ptr(out), _ptr(lse), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(q.device)))
     return (out, lse) if return_lse else out
 
 

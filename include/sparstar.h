@@ -167,6 +167,26 @@ sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const
 sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const void* k,
                                const void* v, void* out, float* lse, void* stream);
 
+/* Bytes of device workspace sparstar_bsa_fwd_balanced needs: 4 * B*H*8*ceil(n_q/8);
+ * -1 if the problem is invalid. */
+int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p);
+
+/* sparstar_bsa_fwd for block lists of uneven length (section 5 "Forward-Only Sparse
+ * Execution": the lists are per query block and their lengths are the caller's).
+ * The attention runs the query blocks of a head in 8 segments, one per XCD, heads in
+ * order; here the rows of each segment are first ordered by list length, longest
+ * first and stably (equal lengths keep their order), into `workspace` (a device
+ * buffer of at least sparstar_balance_workspace_bytes, owned by the caller; on return
+ * it holds the order: entry (b*H + h)*8*ceil(n_q/8) + x*ceil(n_q/8) + m is the query
+ * block of the m-th row of segment x, -1 past the segment's end), so that no long row
+ * is started last.  Every row is computed exactly as by sparstar_bsa_fwd: the outputs
+ * are the same, bit for bit.  SPARSTAR_ERR_CAPACITY if the workspace is too small.
+ * Two calls must not share a workspace while either runs. */
+sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void* q, const void* k,
+                                          const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                                          int64_t col_idx_len, void* out, float* lse, void* workspace,
+                                          int64_t workspace_bytes, void* stream);
+
 /* ---------------- retained attention mass (the pages' quality measure of a selection) ---
  * Section 4 "Analysis" (Figure 3; "Pattern Persistence across Clip Boundaries")
  * and section 1 measure a selection by the share of each query's dense softmax

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 17
+    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 19
     assert {"sparstar_block_mass", "sparstar_selection_mass", "sparstar_window_scores",
             "sparstar_token_topk_mass"} <= set(names)
     L = ctypes.CDLL(S.LIB_PATH)
@@ -180,6 +180,13 @@ def test_mass_entry_points_validate_before_any_device_call():
     assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, None, 4, 0, 0, b, None) == S.ERR_NULL
     assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, ctypes.c_void_p(BOGUS + 4), 4, 0, 0, b,
                                       None) == S.ERR_LAYOUT
+    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p)) == 16 * 40 * 4
+    assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, 10, b, None, None, 1 << 20, None) \
+        == S.ERR_NULL
+    assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, 10, b, None, b, 16 * 40 * 4 - 1, None) \
+        == S.ERR_CAPACITY
+    assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, -1, b, None, b, 1 << 20, None) \
+        == S.ERR_SHAPE
     # nothing listed: nothing to do, no device needed
     assert L.sparstar_token_topk_mass(ctypes.byref(p), None, None, None, None, 0, 0, 0, None, None) == S.OK
 

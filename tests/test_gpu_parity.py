@@ -331,6 +331,59 @@ def test_irregular_csr(D, b, dtype):
             assert np.max(np.abs(got_l[s:e] - l_ref)) < LSE_BF16
 
 
+@pytest.mark.parametrize("D,b,dtype", [(128, 128, torch.bfloat16), (128, 64, torch.bfloat16),
+                                       (128, 256, torch.bfloat16), (64, 64, torch.float32)])
+def test_balanced_equals_plain_bitwise(D, b, dtype):
+    """Rows started longest list first give the same outputs, bit for bit, as the plain call:
+    uneven random lists plus the irregular kinds (empty, duplicates, out of range)."""
+    L_text, L_ref, L_q, H = 64, 900, 1000, 3
+    print_case("balanced", D, b, dtype)
+    Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, D, dtype, seed=12)
+    scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(D))
+    nq, nk = O.num_blocks(L_q, b), O.num_blocks(L_text + L_ref + L_q, b)
+    rng = np.random.default_rng(8)
+    lists = []
+    for r in range(H * nq):
+        if r % 7 == 0:
+            lists.append(np.zeros(0, dtype=np.int64))
+        elif r % 7 == 1:
+            lists.append(np.array([2, 2, -5, nk + 3]))
+        else:
+            lists.append(np.sort(rng.choice(nk, rng.integers(1, nk + 1), replace=False)))
+    rp = np.zeros(len(lists) + 1, dtype=np.int32)
+    rp[1:] = np.cumsum([len(x) for x in lists])
+    rp_t = torch.from_numpy(rp).to(DEV)
+    ci_t = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(DEV)
+    a, la = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True)
+    per = -(-nq // 8)
+    ws = torch.full((H * 8 * per,), -7, dtype=torch.int32, device=DEV)
+    c, lc = S.sparstar_bsa_fwd_balanced(Q, K, V, rp_t, ci_t, scale, return_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c) and torch.equal(la, lc)
+    order = ws.cpu().numpy().reshape(H, 8, per)
+    lens = np.diff(rp).reshape(H, nq)
+    for h in range(H):
+        for x in range(8):
+            seg = order[h, x]
+            blocks = list(range(x * per, min((x + 1) * per, nq)))
+            got = seg[:len(blocks)]
+            assert sorted(got.tolist()) == blocks and np.all(seg[len(blocks):] == -1)
+            ln = lens[h, got]
+            assert np.all(np.diff(ln) <= 0)                      # longest first
+            for u in range(len(got) - 1):                       # stable among equal lengths
+                if ln[u] == ln[u + 1]:
+                    assert got[u] < got[u + 1]
+
+
+def test_balanced_on_the_selection():
+    cfg = I.S192P
+    Q, K, V = inputs(cfg)
+    (out, lse), (_, rp, ci) = S.scale_forward(Q, K, V, scale_of(cfg), 0.3, return_lse=True)
+    c, lc = S.sparstar_bsa_fwd_balanced(Q, K, V, rp, ci, scale_of(cfg), return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, c) and torch.equal(lse, lc)
+
+
 @pytest.mark.parametrize("order", ["rising", "falling"])
 def test_bsa_reference_max_jumps(order):
     """Key blocks whose scores sit far above those of the first block a row
