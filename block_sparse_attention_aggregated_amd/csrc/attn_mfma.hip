@@ -257,7 +257,12 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
     const char* first = base + (size_t)(uint32_t)(s.j * BK + s.h * SUB) * stride_b;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(first), (short)0, (int)((uint32_t)s.len * stride_b), kBufferFlags);
-    lds_char* const ldsb = buf + 4 * wave * (HD * 2);
+    // The per-wavefront LDS offset is hidden from the optimiser here so that the
+    // M0 values are formed in the loop by one scalar add each, rather than hoisted
+    // out of it (where they would be spilled to vector-register lanes).
+    uint32_t woff = 4u * wave * (HD * 2);
+    asm volatile("" : "+s"(woff));
+    lds_char* const ldsb = buf + woff;
   #pragma unroll
     for (int t = 0; t < kPasses; ++t)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ldsb + t * 4 * kWaves * (HD * 2), 16, off[t], 0, 0, 0);
@@ -481,13 +486,20 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
     step(std::integral_constant<int, 1>());
   }
 
-  // Epilogue: the two lanes of a query hold partial row sums of disjoint keys.
+  // Epilogue: the two lanes of a query hold partial row sums of disjoint keys.  The
+  // output pointer, strides and scale are read again from the kernel arguments
+  // (the empty asm hides where the pointer came from), so that they need not stay
+  // in scalar registers through the loop.
+  typedef const __attribute__((address_space(4))) AttnArgs* args_ptr;
+  args_ptr ap = (args_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ap));
+  const int bo = (int)(bh / ap->g.H), ho = (int)(bh - (int64_t)bo * ap->g.H);
   const float l_tot = l + __shfl_xor(l, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const float le = kLse ? l_exact + __shfl_xor(l_exact, 32) : 0.f;
   if (q_valid) {
     if (kOutBf16) {
-      __bf16* orow = static_cast<__bf16*>(a.out) + bi * a.os_b + hi * a.os_h + qrow * a.os_t;
+      __bf16* orow = static_cast<__bf16*>(ap->out) + bo * ap->os_b + ho * ap->os_h + qrow * ap->os_t;
 #pragma unroll
       for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
@@ -499,7 +511,7 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
           *reinterpret_cast<bf16x4*>(orow + dt * 32 + gq * 8 + hl * 4) = v4;
         }
     } else {
-      float* orow = static_cast<float*>(a.out) + bi * a.os_b + hi * a.os_h + qrow * a.os_t;
+      float* orow = static_cast<float*>(ap->out) + bo * ap->os_b + ho * ap->os_h + qrow * ap->os_t;
 #pragma unroll
       for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
@@ -509,7 +521,7 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
           *reinterpret_cast<float4*>(orow + dt * 32 + gq * 8 + hl * 4) = v4;
         }
     }
-    if (kLse && hl == 0) a.lse[bh * g.L_q + qrow] = le > 0.f ? m_run * a.sigma + __logf(le) : -INFINITY;
+    if (kLse && hl == 0) ap->lse[bh * ap->g.L_q + qrow] = le > 0.f ? m_run * ap->sigma + __logf(le) : -INFINITY;
   }
 }
 
