@@ -529,6 +529,36 @@ def test_block_sizes_end_to_end(name, heads, nsample):
     assert torch.equal(a, d)
 
 
+# ---------------------------------------------------------------- graph capture
+
+def test_step_captured_in_a_graph_replays_exactly():
+    """The whole step (pool + score, select, attention) launches no allocation, memset or
+    synchronisation, so it can be captured in a HIP graph: every replay, with eager work on
+    the same buffers in between, equals the eager step bit for bit."""
+    cfg = I.S192P
+    sc = scale_of(cfg)
+    Q, K, V = inputs(cfg)
+    ref, (ref_s, ref_rp, ref_ci) = S.scale_forward(Q, K, V, sc, 0.3)
+    qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, 0.3)
+    out = torch.empty_like(Q)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.sparstar_pool_score(Q, K, sc, qp, kp, scores)
+        S.sparstar_select_blocks(scores, Q, K, sc, 0.3, row_ptr=rp, col_idx=ci)
+        S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, out=out)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        scores.zero_()
+        ci.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(scores, ref_s) and torch.equal(rp, ref_rp) and torch.equal(ci, ref_ci), rep
+        assert torch.equal(out, ref), rep
+
+
 # ---------------------------------------------------------------- full size (sampled)
 
 @pytest.mark.slow
