@@ -81,13 +81,11 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-constexpr int SUB = 64;            // keys per LDS sub-tile (half a key block)
 
-// LDS: two K and two V sub-tile buffers, each [64 keys][256 B] row-major.  They
+// LDS: two K and two V sub-tile buffers, each [SUB keys][256 B] row-major.  They
 // are four separate objects, and every LDS address below is derived from one of
 // them, so the compiler can tell that a read of one buffer does not depend on
 // the direct-to-LDS loads still in flight into another.
-constexpr int kTile = SUB * HD * 2;    // 16 KB
 typedef __attribute__((address_space(3))) char lds_char;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -98,16 +96,20 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
-// Block size kB (queries and keys): kB / 32 wavefronts, two workgroups per CU
-// (one at kB = 256, whose 8 wavefronts already fill the two slots of every SIMD).
+// Block size kB (queries and keys): kB / 32 wavefronts, sub-tiles of SUB keys.
+// kB = 128: 4 wavefronts, 64-key sub-tiles (64 KB of LDS), two workgroups per CU;
+// kB = 256: 8 wavefronts, one workgroup per CU; kB = 64: 2 wavefronts and 32-key
+// sub-tiles (32 KB of LDS), four workgroups per CU.  Every case runs two
+// wavefronts per SIMD.
 template <int kB>
 struct Shape {
   static constexpr int BQ = kB, BK = kB;
   static constexpr int kWaves = kB / 32;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kPerCu = kB == 256 ? 1 : 2;
-  static constexpr int kSubs = kB / 64;      // 64-key sub-tiles per key block
-  static constexpr int kPasses = 16 / kWaves;  // load passes of 4 rows per wavefront per sub-tile
+  static constexpr int SUB = kB == 64 ? 32 : 64;   // keys per LDS sub-tile
+  static constexpr int kPerCu = kB == 256 ? 1 : (kB == 64 ? 4 : 2);
+  static constexpr int kSubs = kB / SUB;           // sub-tiles per key block
+  static constexpr int kPasses = SUB / (4 * kWaves);  // load passes of 4 rows per wavefront per sub-tile
 };
 
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
@@ -115,6 +117,11 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
   constexpr int BQ = Shape<kB>::BQ, BK = Shape<kB>::BK;
   constexpr int kThreads = Shape<kB>::kThreads, kWaves = Shape<kB>::kWaves;
   constexpr int kSubs = Shape<kB>::kSubs, kPasses = Shape<kB>::kPasses;
+  constexpr int SUB = Shape<kB>::SUB;
+  constexpr int kTile = SUB * HD * 2;              // bytes per sub-tile buffer
+  constexpr int NT = SUB / 32;                     // 32-key S tiles per sub-tile
+  constexpr int N1 = 8 * NT;                       // S MFMAs (and softmax pairs) per sub-tile
+  constexpr int N2 = SUB / 4;                      // P.V MFMAs per sub-tile
   __shared__ __attribute__((aligned(16))) char k_lds0[kTile];
   __shared__ __attribute__((aligned(16))) char k_lds1[kTile];
   __shared__ __attribute__((aligned(16))) char v_lds0[kTile];
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     bf16x8 kf[3], vf[3];
     kf[0] = k_frag(k_nxt, 0, 0);
-    kf[1] = k_frag(k_nxt, 1, 0);
+    kf[1] = k_frag(k_nxt, 1 % NT, 1 / NT);
     PTile pu;
     float rs0 = 0.f, rs1 = 0.f, le_t = 0.f;
     // The softmax of pair i runs in three stages over three iterations (FMA in
@@ -427,14 +434,14 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
     };
     f32x2 x_1 = st_a(1), e_0 = st_b(st_a(0));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) kf[(i + 2) % 3] = k_frag(k_nxt, (i + 2) & 1, (i + 2) >> 1);
-      else vf[i - 14] = v_frag(v_cur, i - 14, 0);
-      const int kt = i & 1, ks = i >> 1;
+    for (int i = 0; i < N1; ++i) {
+      if (i + 2 < N1) kf[(i + 2) % 3] = k_frag(k_nxt, (i + 2) % NT, (i + 2) / NT);
+      else vf[i - (N1 - 2)] = v_frag(v_cur, i - (N1 - 2), 0);
+      const int kt = i % NT, ks = i / NT;
       s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], ks == 0 ? f32x16{} : s_nxt[kt], 0,
                                                           0, 0);
-      const f32x2 x_2 = i + 2 < 16 ? st_a(i + 2) : f32x2{};
-      const f32x2 e_1 = i + 1 < 16 ? st_b(x_1) : f32x2{};
+      const f32x2 x_2 = i + 2 < N1 ? st_a(i + 2) : f32x2{};
+      const f32x2 e_1 = i + 1 < N1 ? st_b(x_1) : f32x2{};
       if (kLse) le_t += e_0[0] + e_0[1];
       pu.q[i] = __builtin_convertvector(e_0, bf16x2);
       if (i < 8) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pu.q[i], ones, rs0, false);
@@ -445,7 +452,10 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
     }
     // Keep the softmax above in phase 1: without this, the compiler sinks it past
     // the branches below, next to its first use.
-    asm volatile("" : "+v"(pu.v[0]), "+v"(pu.v[1]), "+v"(pu.v[2]), "+v"(pu.v[3]), "+v"(rs0), "+v"(rs1));
+    if constexpr (NT == 2)
+      asm volatile("" : "+v"(pu.v[0]), "+v"(pu.v[1]), "+v"(pu.v[2]), "+v"(pu.v[3]), "+v"(rs0), "+v"(rs1));
+    else
+      asm volatile("" : "+v"(pu.v[0]), "+v"(pu.v[1]), "+v"(rs0), "+v"(rs1));
     if (__any(rs0 + rs1 >= kBig)) {
       const float m_new = fmaxf(m_run, tile_max(s_cur));
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
@@ -458,7 +468,7 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
       m_run = m_new;
       rs0 = rs1 = le_t = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p_pair(s_cur, i, m_run * c, pu, rs0, rs1, le_t);
+      for (int i = 0; i < N1; ++i) p_pair(s_cur, i, m_run * c, pu, rs0, rs1, le_t);
     }
     l += rs0 + rs1;
     if (kLse) l_exact += le_t;
@@ -466,8 +476,8 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
 
     // Phase 2.  MFMA i: feature tile i & 3, key step i >> 2.
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) vf[(i + 2) % 3] = v_frag(v_cur, (i + 2) & 3, (i + 2) >> 2);
+    for (int i = 0; i < N2; ++i) {
+      if (i + 2 < N2) vf[(i + 2) % 3] = v_frag(v_cur, (i + 2) & 3, (i + 2) >> 2);
       const int dt = i & 3, ks = i >> 2;
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pu.v[ks], o[dt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
