@@ -1,0 +1,52 @@
+"""The benchmark's command-line contract, checked without a GPU: more than one GPU is
+refused with a message before anything touches a device, and the options parse."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=120, cwd=ROOT)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_help_lists_the_modes():
+    r = _run("--help")
+    assert r.returncode == 0
+    for opt in ("--workload", "--density", "--dense", "--mass", "--uneven", "--balanced", "--no-cpu-baseline",
+                "--steps", "--warmup"):
+        assert opt in r.stdout, opt
+
+
+def test_sequence_and_scale_names_resolve():
+    sys.path.insert(0, ROOT)
+    import bench
+    from block_sparse_attention_aggregated_amd import inputs as I
+    assert [c.name for c in bench.workload_configs("clip1")] == [c.name for c in I.CLIP1]
+    assert bench.workload_configs("720p")[0] is I.S720P
+    assert len(bench.workload_configs("sweep")) == 4
+
+
+def test_uneven_lists_recipe():
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import bench
+    rp, ci, counts = bench.uneven_lists(50, 40, 3, 10, seed=1)
+    assert rp[0] == 0 and rp[-1] == len(ci) and np.all(np.diff(rp) == counts + 3)
+    for r in range(50):
+        row = ci[rp[r]:rp[r + 1]]
+        assert list(row[:3]) == [0, 1, 2] and np.all(np.diff(row) > 0) and row.max() < 40
+    assert 1 <= counts.min() and counts.max() <= 19
+    _, _, even = bench.uneven_lists(50, 40, 3, 10, seed=1, even=True)
+    assert np.all(even == 10)
+    order = bench.dispatch_order(1, 2, 11)
+    assert sorted(order.tolist()) == list(range(22))
