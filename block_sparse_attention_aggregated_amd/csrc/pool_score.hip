@@ -8,8 +8,9 @@
 //
 // pool_kernel is a pure HBM stream: each workgroup reads one block of b
 // tokens x D features (32 KB for bf16, b = D = 128) with 16-byte loads, each
-// 16-lane group covering one 256-byte token row, and reduces the rows in
-// float32 through cross-lane shuffles and a small LDS exchange.
+// 16-lane group covering one 256-byte token row (128 rows per pass, two passes
+// at b = 256); each thread sums its rows in float32 and a small LDS exchange
+// sums the row groups.
 // score_kernel is a small float32 GEMM per (batch, head) on the float32
 // matrix cores: 64 x 128 output tiles, K = D.
 
