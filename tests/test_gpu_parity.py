@@ -529,6 +529,52 @@ def test_block_sizes_end_to_end(name, heads, nsample):
     assert torch.equal(a, d)
 
 
+# ---------------------------------------------------------------- seeded random shapes
+
+def _random_cases(n=12, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        b = int(rng.choice([64, 128, 256]))
+        f32 = i % 4 == 3
+        cases.append(dict(L_text=int(rng.integers(0, 600)), L_ref=int(rng.integers(0, 2500)),
+                          L_q=int(rng.integers(1, 2500)), H=int(rng.integers(1, 4)), D=64 if f32 else 128, b=b,
+                          dtype=torch.float32 if f32 else torch.bfloat16, rho=float(rng.uniform(0.05, 1.0)),
+                          policy=int(rng.integers(0, 2)), seed=100 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"b{c['b']}_q{c['L_q']}_p{c['policy']}")
+def test_random_shapes_end_to_end(case):
+    """Seeded random segment lengths, block sizes, densities and policies: selection
+    (near-tie rule) and attention against the oracle, every row."""
+    c = case
+    print_case("random shape", c)
+    Q, K, V = _custom_inputs(c["L_text"], c["L_ref"], c["L_q"], c["H"], c["D"], c["dtype"], seed=c["seed"])
+    sigma = 1 / math.sqrt(c["D"])
+    scale = S.Scale(c["L_text"], c["L_ref"], c["b"], sigma)
+    (out, lse), (scores, rp, ci) = S.scale_forward(Q, K, V, scale, c["rho"], policy=c["policy"],
+                                                   out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    b = c["b"]
+    nq = O.num_blocks(c["L_q"], b)
+    R, C = O.retained_and_candidates(c["L_text"], c["L_ref"], c["L_q"], b, c["policy"])
+    kk = O.budget(len(C), c["rho"])
+    lists = csr_rows(rp, ci)
+    tol = BF16_MAX_ABS if c["dtype"] == torch.bfloat16 else F32_MAX_ABS
+    for h in range(c["H"]):
+        q, k, v = head_np(Q, h), head_np(K, h), head_np(V, h)
+        S_ref = O.block_scores(O.pool_blocks(q, b), O.pool_blocks(k, b), sigma)
+        ref_sets = O.select_blocks(S_ref, R, C, kk)
+        got, got_l = to_f64(out[0, h]), to_f64(lse[0, h])
+        for i in range(nq):
+            compare_row_selection(lists[h * nq + i], ref_sets[i], S_ref[i], len(R), kk)
+            s, e = O.block_range(i, c["L_q"], b)
+            o_ref, l_ref, _ = O.attend_row(q[s:e], k, v, list(lists[h * nq + i]), b, sigma)
+            assert np.max(np.abs(got[s:e] - o_ref)) <= tol, (h, i)
+            assert np.max(np.abs(got_l[s:e] - l_ref)) < LSE_BF16, (h, i)
+
+
 # ---------------------------------------------------------------- graph capture
 
 def test_step_captured_in_a_graph_replays_exactly():
