@@ -100,20 +100,20 @@ constexpr int kBufferFlags = 0x00020000;
 // kB = 128: 4 wavefronts, 64-key sub-tiles (64 KB of LDS), two workgroups per CU;
 // kB = 256: 8 wavefronts, one workgroup per CU; kB = 64: 2 wavefronts and 32-key
 // sub-tiles (32 KB of LDS), four workgroups per CU.  Every case runs two
-// wavefronts per SIMD.
+// wavefronts per SIMD (the second launch-bounds argument is waves per SIMD).
 template <int kB>
 struct Shape {
   static constexpr int BQ = kB, BK = kB;
   static constexpr int kWaves = kB / 32;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int SUB = kB == 64 ? 32 : 64;   // keys per LDS sub-tile
-  static constexpr int kPerCu = kB == 256 ? 1 : (kB == 64 ? 4 : 2);
+  static constexpr int kWavesPerSimd = 2;
   static constexpr int kSubs = kB / SUB;           // sub-tiles per key block
   static constexpr int kPasses = SUB / (4 * kWaves);  // load passes of 4 rows per wavefront per sub-tile
 };
 
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
-__global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_mfma_kernel(AttnArgs a, int per_xcd) {
+__global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void attn_mfma_kernel(AttnArgs a, int per_xcd) {
   constexpr int BQ = Shape<kB>::BQ, BK = Shape<kB>::BK;
   constexpr int kThreads = Shape<kB>::kThreads, kWaves = Shape<kB>::kWaves;
   constexpr int kSubs = Shape<kB>::kSubs, kPasses = Shape<kB>::kPasses;
@@ -180,36 +180,42 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
     if (beg < 0) beg = 0;
     if ((int64_t)end > a.col_idx_len) end = (int)a.col_idx_len;
   }
-  auto next_valid = [&](int p) -> int {
+  // A sub-tile: sub-tile h of key block j at list position p; len real keys (1..SUB).
+  struct Sub {
+    int p, j, h, len, jn;  // jn: the list entry at p + 1, read ahead (or -1)
+  };
+  auto sub_at = [&](int p, int j, int h) -> Sub {
+    Sub s;
+    s.p = p;
+    s.h = h;
+    s.j = p < end ? j : 0;
+    s.len = p < end ? min(SUB, (int)g.L_k - s.j * BK - h * SUB) : 0;
+    s.jn = -1;
+    return s;
+  };
+  // First sub-tile of the first in-range list entry at or after p; each entry is
+  // read once.
+  auto first_sub = [&](int p) -> Sub {
+    int j = (int)p;
     if (!kDense) {
+      j = 0;
       while (p < end) {
-        const int j = ci[p];
+        j = ci[p];
         if (j >= 0 && j < g.n_k) break;
         ++p;
       }
     }
-    return p;
-  };
-  // A sub-tile: half h of key block j at list position p; len real keys (1..64).
-  struct Sub {
-    int p, j, h, len;
-  };
-  auto make_sub = [&](int p, int h) -> Sub {
-    Sub s;
-    s.p = p;
-    s.h = h;
-    s.j = p < end ? (kDense ? (int)p : ci[p]) : 0;
-    s.len = p < end ? min(SUB, (int)g.L_k - s.j * BK - h * SUB) : 0;
-    return s;
+    return sub_at(p, j, 0);
   };
   auto advance = [&](const Sub& s) -> Sub {
     if (s.p >= end) return s;
-    if constexpr (kSubs == 2) {
-      if (s.h == 0 && (int)g.L_k - s.j * BK > SUB) return make_sub(s.p, 1);
-    } else if constexpr (kSubs > 2) {
-      if (s.h + 1 < kSubs && (int)g.L_k - s.j * BK > (s.h + 1) * SUB) return make_sub(s.p, s.h + 1);
+    if (s.h + 1 < kSubs && (int)g.L_k - s.j * BK > (s.h + 1) * SUB) {
+      Sub r = sub_at(s.p, s.j, s.h + 1);
+      if (!kDense) r.jn = s.h + 2 == kSubs && s.p + 1 < end ? ci[s.p + 1] : s.jn;
+      return r;
     }
-    return make_sub(next_valid(s.p + 1), 0);
+    if (!kDense && s.jn >= 0 && s.jn < g.n_k) return sub_at(s.p + 1, s.jn, 0);
+    return first_sub(s.p + 1);
   };
 
   // K and V staging (direct to LDS): wavefront w, load pass t (0 .. kPasses - 1)
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kPerCu) void attn_m
     }
   }
   __syncthreads();
-  Sub cur = make_sub(next_valid(beg), 0);
+  Sub cur = first_sub(beg);
   Sub nxt = advance(cur);
   if (cur.p < end) {
     load_k(cur, kb[0]);
