@@ -285,10 +285,13 @@ def test_ragged_shapes(L_text, L_ref, L_q, H, D, b, dtype, rho):
             assert np.max(np.abs(to_f64(lse[0, h])[s:e] - ref_l[i])) < LSE_BF16
 
 
-@pytest.mark.parametrize("D,b,dtype", [(128, 128, torch.bfloat16), (64, 64, torch.float32)])
+@pytest.mark.parametrize("D,b,dtype", [(128, 128, torch.bfloat16), (128, 64, torch.bfloat16),
+                                       (128, 256, torch.bfloat16), (64, 64, torch.float32)])
 def test_irregular_csr(D, b, dtype):
     """Uneven block lists: empty rows, one block, every block, duplicates and
-    out-of-range indices (skipped), rows in any order."""
+    out-of-range indices (skipped, also right after a valid entry, where the
+    kernel has read the next entry ahead), rows in any order; the last key
+    block is partial at every block size."""
     L_text, L_ref, L_q, H = 64, 700, 600, 2
     print_case("irregular csr", D, b, dtype)
     Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, D, dtype, seed=11)
