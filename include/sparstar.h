@@ -139,6 +139,9 @@ sparstar_status sparstar_pool_score(const sparstar_problem* p, const void* q, co
  *   row_ptr  : out, int32 [B*H*n_q + 1]; row_ptr[r] = r * (r_keep + k).
  *   col_idx  : out, int32 [col_idx_capacity]; the first sparstar_select_nnz entries
  *              are written.  SPARSTAR_ERR_CAPACITY if the capacity is smaller.
+ * One wavefront ranks a row with its candidates held in registers: at most 4,096
+ * candidate blocks per row (n_k - r_keep), SPARSTAR_ERR_UNSUPPORTED beyond.  The
+ * total nnz must fit int32 (SPARSTAR_ERR_SHAPE otherwise).
  * NaN scores are not supported (their rank is unspecified). */
 sparstar_status sparstar_select_blocks(const sparstar_problem* p, const float* scores,
                                        double density, int32_t policy, int32_t* row_ptr,
