@@ -183,7 +183,10 @@ int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p);
  * it holds the order: entry (b*H + h)*8*ceil(n_q/8) + x*ceil(n_q/8) + m is the query
  * block of the m-th row of segment x, -1 past the segment's end), so that no long row
  * is started last.  Every row is computed exactly as by sparstar_bsa_fwd: the outputs
- * are the same, bit for bit.  SPARSTAR_ERR_CAPACITY if the workspace is too small.
+ * are the same, bit for bit.  The order is used by the bf16 MFMA kernel; the float32
+ * kernel (float32 inputs, D = 64, or K/V extents of 2^31 bytes or more per head) runs
+ * the rows in their natural order, and the workspace is still written.
+ * SPARSTAR_ERR_CAPACITY if the workspace is too small.
  * Two calls must not share a workspace while either runs. */
 sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void* q, const void* k,
                                           const void* v, const int32_t* row_ptr, const int32_t* col_idx,
