@@ -611,10 +611,12 @@ def test_step_captured_in_a_graph_replays_exactly():
 # ---------------------------------------------------------------- full size (sampled)
 
 @pytest.mark.slow
-@pytest.mark.parametrize("cfg,rho", [(I.S720P, 0.2), (I.SWEEP[0], 0.2)])
+@pytest.mark.parametrize("cfg,rho", [(I.S720P, 0.2), (I.SWEEP[0], 0.2), (I.S720P_B64, 0.2), (I.S720P_B256, 0.2)],
+                         ids=lambda x: getattr(x, "name", str(x)))
 def test_full_size_sampled(cfg, rho):
     """The timed launch configuration at full size: selection on every row of sampled heads,
-    attention on sampled query blocks (first, last partial, random)."""
+    attention on sampled query blocks (first, last partial, random); also the 720p scale at
+    the block sizes 64 and 256 of the pages' ablation."""
     print_case("full size", cfg.name, rho)
     Q, K, V = inputs(cfg)
     (out, lse), (sc, rp, ci) = S.scale_forward(Q, K, V, scale_of(cfg), rho, return_lse=True)
