@@ -146,7 +146,10 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (n_cand <= 64 * 4) launch_t<4>(a, s);
   else if (n_cand <= 64 * 8) launch_t<8>(a, s);
   else if (n_cand <= 64 * 16) launch_t<16>(a, s);
+  else if (n_cand <= 64 * 24) launch_t<24>(a, s);
   else if (n_cand <= 64 * 32) launch_t<32>(a, s);
+  else if (n_cand <= 64 * 40) launch_t<40>(a, s);
+  else if (n_cand <= 64 * 48) launch_t<48>(a, s);
   else if (n_cand <= 64 * 64) launch_t<64>(a, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
