@@ -238,16 +238,19 @@ def run_mass(args):
             f.write(line + "\n")
 
 
-def dispatch_order(B, H, n_q, xcds=8):
+def dispatch_order(B, H, n_q, xcds=8, segments=4):
     """Rows in the order bsa_fwd's workgroups are numbered: workgroup w = 8 m + x runs query block
-    x * ceil(n_q/8) + m % ceil(n_q/8) of head m // ceil(n_q/8) (a workgroup past n_q exits)."""
-    per = -(-n_q // xcds)
+    s * per + m % per of head 2 (m // per) + x // 4, with s = x % 4 and per = ceil(n_q / 4) (a
+    workgroup past n_q or past the last head exits)."""
+    per = -(-n_q // segments)
+    at_once = xcds // segments
     order = []
-    for w in range(B * H * per * xcds):
+    for w in range(-(-(B * H) // at_once) * per * xcds):
         m, x = divmod(w, xcds)
-        bh, qi = divmod(m, per)
-        qi += x * per
-        if qi < n_q:
+        hset, mm = divmod(m, per)
+        bh = hset * at_once + x // segments
+        qi = (x % segments) * per + mm
+        if bh < B * H and qi < n_q:
             order.append(bh * n_q + qi)
     return np.array(order)
 

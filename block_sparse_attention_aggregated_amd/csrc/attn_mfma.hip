@@ -46,13 +46,15 @@
 // read through the scalar cache.
 //
 // Workgroups are mapped to rows XCD-aware (with a row order for uneven lists,
-// each XCD starts the rows of its segment of a head longest list first).  Consecutive workgroup ids are
-// dispatched round-robin over the 8 XCDs; XCD x takes query blocks
-// [x * per_xcd, (x + 1) * per_xcd) of each head, per_xcd = ceil(n_q / 8), and
-// all XCDs go through the heads in the same order.  The workgroups resident on
-// one XCD are then consecutive query blocks of one head, whose block lists
-// overlap and share that XCD's L2; and at any time the whole GPU works on one
-// or two heads, whose K and V fit the Infinity Cache, so L2 misses are served
+// each XCD starts the rows of its segment of a head longest list first).  Consecutive
+// workgroup ids are dispatched round-robin over the 8 XCDs.  A head's query blocks
+// are split into 4 contiguous segments of per = ceil(n_q / 4) blocks; XCD x takes
+// segment x % 4 of the even (x < 4) or odd (x >= 4) head of each pair, pairs in
+// order.  The workgroups resident on one XCD are then consecutive query blocks of
+// one head, whose block lists overlap and share that XCD's L2 (segments of n_q / 4
+// rather than n_q / 8 blocks: the 64 resident workgroups straddle two heads less
+// often); and the GPU works on two heads at a time (four briefly, where one pair
+// follows the next), whose K and V fit the Infinity Cache, so L2 misses are served
 // there rather than by HBM.
 
 #include "sparstar_internal.h"
@@ -68,7 +70,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int HD = 128;            // head_dim
-constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kBig = 18446744073709551616.0f;  // 2^64: bound on a lane's P sum per sub-tile
 
@@ -113,7 +114,7 @@ struct Shape {
 };
 
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
-__global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void attn_mfma_kernel(AttnArgs a, int per_xcd) {
+__global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void attn_mfma_kernel(AttnArgs a, int per) {
   constexpr int BQ = Shape<kB>::BQ, BK = Shape<kB>::BK;
   constexpr int kThreads = Shape<kB>::kThreads, kWaves = Shape<kB>::kWaves;
   constexpr int kSubs = Shape<kB>::kSubs, kPasses = Shape<kB>::kPasses;
@@ -130,14 +131,18 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
   lds_char* const vb[2] = {(lds_char*)v_lds0, (lds_char*)v_lds1};
 
   const Geometry& g = a.g;
-  // Workgroup id -> (head, query block): XCD x = id % 8 takes query blocks
-  // [x * per_xcd, (x + 1) * per_xcd) of every head, heads in order.
-  // With a row order (uneven lists), the m-th workgroup of segment (head, XCD) runs the
+  // Workgroup id -> (head, query block): XCD x = id % 8 takes the query blocks
+  // [s * per, (s + 1) * per) of segment s = x % kSegments of head
+  // 2 j + x / kSegments (kXcds / kSegments = 2 heads at a time), heads in order.
+  // With a row order (uneven lists), the m-th workgroup of segment (head, s) runs the
   // segment's m-th longest row instead of its m-th.
   const int64_t k = blockIdx.x / kXcds;
-  const int64_t bh = k / per_xcd;
-  const int xcd = (int)(blockIdx.x % kXcds), m = (int)(k - bh * per_xcd);
-  const int qi = a.row_order ? a.row_order[(bh * kXcds + xcd) * per_xcd + m] : xcd * per_xcd + m;
+  const int64_t hset = k / per;
+  const int xcd = (int)(blockIdx.x % kXcds), m = (int)(k - hset * per);
+  const int64_t bh = hset * (kXcds / kSegments) + xcd / kSegments;
+  if (bh >= (int64_t)g.B * g.H) return;  // uniform over the workgroup
+  const int seg = xcd % kSegments;
+  const int qi = a.row_order ? a.row_order[(bh * kSegments + seg) * per + m] : seg * per + m;
   if (qi < 0 || qi >= g.n_q) return;  // uniform over the workgroup
   const int64_t row = bh * g.n_q + qi;
   const int bi = (int)(bh / g.H), hi = (int)(bh - (int64_t)bi * g.H);
@@ -543,11 +548,12 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
 
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  const int per_xcd = (a.g.n_q + kXcds - 1) / kXcds;
-  const int64_t grid = (int64_t)a.g.B * a.g.H * per_xcd * kXcds;
+  constexpr int kHeadsAtOnce = kXcds / kSegments;
+  const int per = (a.g.n_q + kSegments - 1) / kSegments;
+  const int64_t grid = ((int64_t)a.g.B * a.g.H + kHeadsAtOnce - 1) / kHeadsAtOnce * per * kXcds;
   if (grid > 0xffffffffll) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_mfma_kernel<kB, kDense, kOutBf16, kLse>), dim3((unsigned)grid),
-                     dim3(Shape<kB>::kThreads), 0, s, a, per_xcd);
+                     dim3(Shape<kB>::kThreads), 0, s, a, per);
   return hipSuccess;
 }
 

@@ -1,21 +1,22 @@
-// Row order for uneven block lists: longest list first, within each head and XCD.
+// Row order for uneven block lists: longest list first, within each segment of a head.
 //
 // The block-sparse attention forward ("SparSTAR: Sparse Attention for
 // SpaceTime AutoRegressive Video Synthesis", section 5 "Forward-Only Sparse
 // Execution") runs one workgroup per query-block row.  Its workgroups are
-// numbered so that XCD x runs the query blocks [x * per, (x + 1) * per) of
-// every head, heads in order (per = ceil(n_q / 8)): the rows in flight belong
-// to one or two heads, whose K and V stay in the Infinity Cache.  With uneven
-// lists the rows handed out last set the tail: a long row started last keeps
-// part of the GPU busy alone.  This kernel reorders the rows of each such
-// segment (one head, one XCD) by list length, longest first (the longest-
-// processing-time order), and keeps the order of heads and XCDs.  The sort is
-// stable, so lists of equal length keep the plain order exactly.
+// numbered so that a head's query blocks form kSegments contiguous segments
+// [x * per, (x + 1) * per) (per = ceil(n_q / kSegments)), each run by one XCD,
+// two heads at a time, heads in order: the rows in flight belong to few heads,
+// whose K and V stay in the Infinity Cache.  With uneven lists the rows handed
+// out last set the tail: a long row started last keeps part of the GPU busy
+// alone.  This kernel reorders the rows of each segment by list length, longest
+// first (the longest-processing-time order), and keeps the order of heads and
+// segments.  The sort is stable, so lists of equal length keep the plain order
+// exactly.
 //
 // One workgroup per segment; each row's rank is the number of rows of the
 // segment with a longer list, or an equally long one and a lower index.
-// order[(bh * 8 + x) * per + m] is the query block of the m-th row of segment
-// (bh, x), or -1 past the segment's end.
+// order[(bh * kSegments + x) * per + m] is the query block of the m-th row of
+// segment (bh, x), or -1 past the segment's end.
 
 #include "sparstar_internal.h"
 
@@ -23,14 +24,13 @@ namespace sparstar {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kXcds = 8;
 
 __global__ __launch_bounds__(kThreads) void row_order_kernel(const int32_t* row_ptr, int32_t n_q, int32_t per,
                                                              int64_t col_idx_len, int32_t* order) {
   extern __shared__ int32_t len[];  // [per]
-  const int64_t seg = blockIdx.x;   // bh * 8 + x
-  const int64_t bh = seg / kXcds;
-  const int x = (int)(seg - bh * kXcds);
+  const int64_t seg = blockIdx.x;   // bh * kSegments + x
+  const int64_t bh = seg / kSegments;
+  const int x = (int)(seg - bh * kSegments);
   const int q0 = x * per;
   const int n = max(0, min(per, n_q - q0));
   for (int m = threadIdx.x; m < n; m += kThreads) {
@@ -57,13 +57,15 @@ __global__ __launch_bounds__(kThreads) void row_order_kernel(const int32_t* row_
 
 }  // namespace
 
-int64_t row_order_entries(int64_t bh, int32_t n_q) { return bh * kXcds * (int64_t)((n_q + kXcds - 1) / kXcds); }
+int64_t row_order_entries(int64_t bh, int32_t n_q) {
+  return bh * kSegments * (int64_t)((n_q + kSegments - 1) / kSegments);
+}
 
 hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int64_t col_idx_len, int32_t* order,
                             hipStream_t s) {
   if (bh == 0 || n_q == 0) return hipSuccess;
-  const int32_t per = (n_q + kXcds - 1) / kXcds;
-  const int64_t segs = bh * kXcds;
+  const int32_t per = (n_q + kSegments - 1) / kSegments;
+  const int64_t segs = bh * kSegments;
   if (segs > 0xffffffffll || (size_t)per * sizeof(int32_t) > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(row_order_kernel, dim3((unsigned)segs), dim3(kThreads), (size_t)per * sizeof(int32_t), s,
                      row_ptr, n_q, per, col_idx_len, order);

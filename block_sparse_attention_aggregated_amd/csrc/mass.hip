@@ -59,7 +59,6 @@ constexpr int kMB = 128;         // block size (queries and keys)
 constexpr int kMD = 128;         // head_dim
 constexpr int kSub = 64;         // keys per LDS sub-tile
 constexpr int kTileBytes = kSub * kMD * 2;
-constexpr int kXcds = 8;
 constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer resource (32-bit data format)
 
 __global__ __launch_bounds__(256, 2) void block_mass_mfma_kernel(MassArgs a, int per_xcd) {

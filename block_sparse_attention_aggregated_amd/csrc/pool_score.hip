@@ -126,7 +126,6 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolScoreArgs a) {
 // Output: register r of a lane holds row 8 (r >> 2) + 4 (l >> 5) + (r & 3) and
 // column l & 31 of its 32 x 32 tile.
 constexpr int kTileI = 64, kTileJ = 128;
-constexpr int kXcds = 8;
 constexpr int kDc = 32;           // features per chunk
 constexpr int kPad = kDc + 4;     // LDS row pitch in floats (144 B: conflict-free 16-byte reads)
 

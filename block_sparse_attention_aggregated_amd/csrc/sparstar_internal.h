@@ -104,8 +104,15 @@ hipError_t launch_selection_mass(const SelMassArgs& a, hipStream_t s);
 hipError_t launch_window_scores(float* out, int64_t bh, int n_q, int n_k, int b, int64_t offset, hipStream_t s);
 hipError_t launch_token_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
-// Query blocks of each (head, XCD) segment ordered by list length, longest first:
-// order[(bh * 8 + x) * ceil(n_q / 8) + m], -1 past a segment's end.
+// Attention row mapping: the query blocks of a head are split into kSegments
+// contiguous segments of ceil(n_q / kSegments) blocks; workgroup id w runs on
+// XCD x = w % kXcds, which takes segment x % kSegments of head
+// (w / kXcds / per) * (kXcds / kSegments) + x / kSegments, so kXcds / kSegments
+// heads are in flight at a time, each on kSegments XCDs.
+constexpr int kXcds = 8;
+constexpr int kSegments = 4;
+// Query blocks of each (head, segment) ordered by list length, longest first:
+// order[(bh * kSegments + x) * ceil(n_q / kSegments) + m], -1 past a segment's end.
 int64_t row_order_entries(int64_t bh, int32_t n_q);
 hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int64_t col_idx_len, int32_t* order,
                             hipStream_t s);
