@@ -238,10 +238,12 @@ def run_mass(args):
             f.write(line + "\n")
 
 
-def dispatch_order(B, H, n_q, xcds=8, segments=4):
-    """Rows in the order bsa_fwd's workgroups are numbered: workgroup w = 8 m + x runs query block
-    s * per + m % per of head 2 (m // per) + x // 4, with s = x % 4 and per = ceil(n_q / 4) (a
-    workgroup past n_q or past the last head exits)."""
+def dispatch_order(B, H, n_q, block, xcds=8):
+    """Rows in the order bsa_fwd's workgroups are numbered: with S segments per head (8 at block
+    64, 4 otherwise) and per = ceil(n_q / S), workgroup w = 8 m + x runs query block
+    (x % S) * per + m % per of head (8 / S) (m // per) + x // S (a workgroup past n_q or past the
+    last head exits)."""
+    segments = 8 if block == 64 else 4
     per = -(-n_q // segments)
     at_once = xcds // segments
     order = []
@@ -312,7 +314,7 @@ def main():
             k = S.blocks_per_row(p, density, cfg.policy) - r
             n_rows = cfg.batch * cfg.heads * S.num_q_blocks(p)
             print(f"# drawing uneven block lists for {n_rows} rows", file=sys.stderr, flush=True)
-            first = dispatch_order(cfg.batch, cfg.heads, S.num_q_blocks(p)) if args.longest_first else None
+            first = dispatch_order(cfg.batch, cfg.heads, S.num_q_blocks(p), cfg.block) if args.longest_first else None
             rp_np, ci_np, counts = uneven_lists(n_rows, S.num_k_blocks(p), r, k, even=args.random_even, first=first)
             rp, ci = torch.from_numpy(rp_np).to(dev), torch.from_numpy(ci_np).to(dev)
             print(f"# candidates per row: min {counts.min()} mean {counts.mean():.1f} max {counts.max()} "

@@ -48,14 +48,15 @@
 // Workgroups are mapped to rows XCD-aware (with a row order for uneven lists,
 // each XCD starts the rows of its segment of a head longest list first).  Consecutive
 // workgroup ids are dispatched round-robin over the 8 XCDs.  A head's query blocks
-// are split into 4 contiguous segments of per = ceil(n_q / 4) blocks; XCD x takes
-// segment x % 4 of the even (x < 4) or odd (x >= 4) head of each pair, pairs in
-// order.  The workgroups resident on one XCD are then consecutive query blocks of
-// one head, whose block lists overlap and share that XCD's L2 (segments of n_q / 4
-// rather than n_q / 8 blocks: the 64 resident workgroups straddle two heads less
-// often); and the GPU works on two heads at a time (four briefly, where one pair
-// follows the next), whose K and V fit the Infinity Cache, so L2 misses are served
-// there rather than by HBM.
+// are split into S contiguous segments of per = ceil(n_q / S) blocks, S = 4 at
+// b = 128 and 256: XCD x takes segment x % 4 of the even (x < 4) or odd (x >= 4)
+// head of each pair, pairs in order; S = 8 at b = 64: XCD x takes segment x of
+// every head.  The workgroups resident on one XCD are then consecutive query
+// blocks of one head, whose block lists overlap and share that XCD's L2; and the
+// GPU works on one or two heads at a time, whose K and V fit the Infinity Cache,
+// so L2 misses are served there rather than by HBM.  (Which S is faster was
+// measured per block size; at b = 128 four segments also cut the traffic beyond
+// L2 by a sixth.)
 
 #include "sparstar_internal.h"
 
@@ -132,17 +133,18 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
 
   const Geometry& g = a.g;
   // Workgroup id -> (head, query block): XCD x = id % 8 takes the query blocks
-  // [s * per, (s + 1) * per) of segment s = x % kSegments of head
-  // 2 j + x / kSegments (kXcds / kSegments = 2 heads at a time), heads in order.
+  // [s * per, (s + 1) * per) of segment s = x % S of head (8 / S) j + x / S, with
+  // S = kSeg segments per head (8 / S heads at a time), heads in order.
   // With a row order (uneven lists), the m-th workgroup of segment (head, s) runs the
   // segment's m-th longest row instead of its m-th.
+  constexpr int kSeg = segments_per_head(kB);
   const int64_t k = blockIdx.x / kXcds;
   const int64_t hset = k / per;
   const int xcd = (int)(blockIdx.x % kXcds), m = (int)(k - hset * per);
-  const int64_t bh = hset * (kXcds / kSegments) + xcd / kSegments;
+  const int64_t bh = hset * (kXcds / kSeg) + xcd / kSeg;
   if (bh >= (int64_t)g.B * g.H) return;  // uniform over the workgroup
-  const int seg = xcd % kSegments;
-  const int qi = a.row_order ? a.row_order[(bh * kSegments + seg) * per + m] : seg * per + m;
+  const int seg = xcd % kSeg;
+  const int qi = a.row_order ? a.row_order[(bh * kSeg + seg) * per + m] : seg * per + m;
   if (qi < 0 || qi >= g.n_q) return;  // uniform over the workgroup
   const int64_t row = bh * g.n_q + qi;
   const int bi = (int)(bh / g.H), hi = (int)(bh - (int64_t)bi * g.H);
@@ -548,8 +550,9 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
 
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  constexpr int kHeadsAtOnce = kXcds / kSegments;
-  const int per = (a.g.n_q + kSegments - 1) / kSegments;
+  constexpr int kSeg = segments_per_head(kB);
+  constexpr int kHeadsAtOnce = kXcds / kSeg;
+  const int per = (a.g.n_q + kSeg - 1) / kSeg;
   const int64_t grid = ((int64_t)a.g.B * a.g.H + kHeadsAtOnce - 1) / kHeadsAtOnce * per * kXcds;
   if (grid > 0xffffffffll) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_mfma_kernel<kB, kDense, kOutBf16, kLse>), dim3((unsigned)grid),

@@ -3,9 +3,9 @@
 // The block-sparse attention forward ("SparSTAR: Sparse Attention for
 // SpaceTime AutoRegressive Video Synthesis", section 5 "Forward-Only Sparse
 // Execution") runs one workgroup per query-block row.  Its workgroups are
-// numbered so that a head's query blocks form kSegments contiguous segments
-// [x * per, (x + 1) * per) (per = ceil(n_q / kSegments)), each run by one XCD,
-// two heads at a time, heads in order: the rows in flight belong to few heads,
+// numbered so that a head's query blocks form S contiguous segments
+// [x * per, (x + 1) * per) (per = ceil(n_q / S), S = segments_per_head(b)), each
+// run by one XCD, heads in order: the rows in flight belong to one or two heads,
 // whose K and V stay in the Infinity Cache.  With uneven lists the rows handed
 // out last set the tail: a long row started last keeps part of the GPU busy
 // alone.  This kernel reorders the rows of each segment by list length, longest
@@ -15,8 +15,8 @@
 //
 // One workgroup per segment; each row's rank is the number of rows of the
 // segment with a longer list, or an equally long one and a lower index.
-// order[(bh * kSegments + x) * per + m] is the query block of the m-th row of
-// segment (bh, x), or -1 past the segment's end.
+// order[(bh * S + x) * per + m] is the query block of the m-th row of segment
+// (bh, x), or -1 past the segment's end.
 
 #include "sparstar_internal.h"
 
@@ -26,11 +26,12 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void row_order_kernel(const int32_t* row_ptr, int32_t n_q, int32_t per,
-                                                             int64_t col_idx_len, int32_t* order) {
+                                                             int32_t segs_per_head, int64_t col_idx_len,
+                                                             int32_t* order) {
   extern __shared__ int32_t len[];  // [per]
-  const int64_t seg = blockIdx.x;   // bh * kSegments + x
-  const int64_t bh = seg / kSegments;
-  const int x = (int)(seg - bh * kSegments);
+  const int64_t seg = blockIdx.x;   // bh * segs_per_head + x
+  const int64_t bh = seg / segs_per_head;
+  const int x = (int)(seg - bh * segs_per_head);
   const int q0 = x * per;
   const int n = max(0, min(per, n_q - q0));
   for (int m = threadIdx.x; m < n; m += kThreads) {
@@ -57,18 +58,20 @@ __global__ __launch_bounds__(kThreads) void row_order_kernel(const int32_t* row_
 
 }  // namespace
 
-int64_t row_order_entries(int64_t bh, int32_t n_q) {
-  return bh * kSegments * (int64_t)((n_q + kSegments - 1) / kSegments);
+int64_t row_order_entries(int64_t bh, int32_t n_q, int32_t b) {
+  const int S = segments_per_head(b);
+  return bh * S * (int64_t)((n_q + S - 1) / S);
 }
 
-hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int64_t col_idx_len, int32_t* order,
-                            hipStream_t s) {
+hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int32_t b, int64_t col_idx_len,
+                            int32_t* order, hipStream_t s) {
   if (bh == 0 || n_q == 0) return hipSuccess;
-  const int32_t per = (n_q + kSegments - 1) / kSegments;
-  const int64_t segs = bh * kSegments;
+  const int32_t S = segments_per_head(b);
+  const int32_t per = (n_q + S - 1) / S;
+  const int64_t segs = bh * S;
   if (segs > 0xffffffffll || (size_t)per * sizeof(int32_t) > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(row_order_kernel, dim3((unsigned)segs), dim3(kThreads), (size_t)per * sizeof(int32_t), s,
-                     row_ptr, n_q, per, col_idx_len, order);
+                     row_ptr, n_q, per, S, col_idx_len, order);
   return hipGetLastError();
 }
 

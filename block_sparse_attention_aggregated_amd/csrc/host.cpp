@@ -467,7 +467,8 @@ sparstar_status sparstar_token_topk_mass(const sparstar_problem* p, const void* 
 
 int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p) {
   if (check_problem_impl(p) != SPARSTAR_OK) return -1;
-  return sparstar::row_order_entries((int64_t)p->batch * p->heads, (int32_t)ceil_div(p->len_q, p->block)) *
+  return sparstar::row_order_entries((int64_t)p->batch * p->heads, (int32_t)ceil_div(p->len_q, p->block),
+                                     p->block) *
          (int64_t)sizeof(int32_t);
 }
 
@@ -486,7 +487,8 @@ sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void*
         (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
       return fail(SPARSTAR_ERR_LAYOUT, "row_ptr, col_idx, lse and workspace must be 4-byte aligned");
     const int64_t rows = (int64_t)a.g.B * a.g.H * a.g.n_q;
-    const int64_t need = sparstar::row_order_entries((int64_t)a.g.B * a.g.H, a.g.n_q) * (int64_t)sizeof(int32_t);
+    const int64_t need =
+        sparstar::row_order_entries((int64_t)a.g.B * a.g.H, a.g.n_q, a.g.b) * (int64_t)sizeof(int32_t);
     if (workspace_bytes < need)
       return fail(SPARSTAR_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
                   (long long)need);
@@ -497,7 +499,7 @@ sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void*
     if (rows == 0) return ok();
     if ((s = check_device()) != SPARSTAR_OK) return s;
     int32_t* order = static_cast<int32_t*>(workspace);
-    s = launched(sparstar::launch_row_order(row_ptr, (int64_t)a.g.B * a.g.H, a.g.n_q, col_idx_len, order,
+    s = launched(sparstar::launch_row_order(row_ptr, (int64_t)a.g.B * a.g.H, a.g.n_q, a.g.b, col_idx_len, order,
                                             (hipStream_t)stream),
                  "row order launch");
     if (s != SPARSTAR_OK) return s;

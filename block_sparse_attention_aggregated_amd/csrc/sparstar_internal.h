@@ -104,18 +104,18 @@ hipError_t launch_selection_mass(const SelMassArgs& a, hipStream_t s);
 hipError_t launch_window_scores(float* out, int64_t bh, int n_q, int n_k, int b, int64_t offset, hipStream_t s);
 hipError_t launch_token_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
-// Attention row mapping: the query blocks of a head are split into kSegments
-// contiguous segments of ceil(n_q / kSegments) blocks; workgroup id w runs on
-// XCD x = w % kXcds, which takes segment x % kSegments of head
-// (w / kXcds / per) * (kXcds / kSegments) + x / kSegments, so kXcds / kSegments
-// heads are in flight at a time, each on kSegments XCDs.
+// Attention row mapping: the query blocks of a head are split into S contiguous
+// segments of per = ceil(n_q / S) blocks; workgroup id w runs on XCD
+// x = w % kXcds, which takes segment x % S of head (w / kXcds / per) * (kXcds / S)
+// + x / S, so kXcds / S heads are in flight at a time, each on S XCDs.  S = 8 at
+// b = 64 and 4 otherwise (measured: each is the faster one at its block size).
 constexpr int kXcds = 8;
-constexpr int kSegments = 4;
+constexpr int segments_per_head(int b) { return b == 64 ? 8 : 4; }
 // Query blocks of each (head, segment) ordered by list length, longest first:
-// order[(bh * kSegments + x) * ceil(n_q / kSegments) + m], -1 past a segment's end.
-int64_t row_order_entries(int64_t bh, int32_t n_q);
-hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int64_t col_idx_len, int32_t* order,
-                            hipStream_t s);
+// order[(bh * S + x) * ceil(n_q / S) + m], -1 past a segment's end.
+int64_t row_order_entries(int64_t bh, int32_t n_q, int32_t b);
+hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int32_t b, int64_t col_idx_len,
+                            int32_t* order, hipStream_t s);
 // bf16 inputs, D = 128, b = 64, 128 or 256, in-head K/V byte offsets below 2^31 (MFMA path).
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 // Any supported shape/dtype (float32 path).

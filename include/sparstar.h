@@ -170,18 +170,20 @@ sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const
 sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const void* k,
                                const void* v, void* out, float* lse, void* stream);
 
-/* Bytes of device workspace sparstar_bsa_fwd_balanced needs: 4 * B*H*4*ceil(n_q/4);
+/* Bytes of device workspace sparstar_bsa_fwd_balanced needs: 4 * B*H*S*ceil(n_q/S),
+ * with S = 8 segments per head at block 64 and 4 at blocks 128 and 256;
  * -1 if the problem is invalid. */
 int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p);
 
 /* sparstar_bsa_fwd for block lists of uneven length (section 5 "Forward-Only Sparse
  * Execution": the lists are per query block and their lengths are the caller's).
- * The attention runs the query blocks of a head in 4 contiguous segments of
- * ceil(n_q/4) blocks, one per XCD, two heads at a time, heads in order; here the rows
- * of each segment are first ordered by list length, longest first and stably (equal
- * lengths keep their order), into `workspace` (a device buffer of at least
+ * The attention runs the query blocks of a head in S contiguous segments of
+ * ceil(n_q/S) blocks, one per XCD (S = 8 at block 64: one head at a time; S = 4 at
+ * blocks 128 and 256: two heads at a time), heads in order; here the rows of each
+ * segment are first ordered by list length, longest first and stably (equal lengths
+ * keep their order), into `workspace` (a device buffer of at least
  * sparstar_balance_workspace_bytes, owned by the caller; on return it holds the
- * order: entry (b*H + h)*4*ceil(n_q/4) + x*ceil(n_q/4) + m is the query block of the
+ * order: entry (b*H + h)*S*ceil(n_q/S) + x*ceil(n_q/S) + m is the query block of the
  * m-th row of segment x, -1 past the segment's end), so that no long row is started
  * last.  Every row is computed exactly as by sparstar_bsa_fwd: the outputs
  * are the same, bit for bit.  The order is used by the bf16 MFMA kernel; the float32

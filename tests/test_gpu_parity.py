@@ -358,15 +358,17 @@ def test_balanced_equals_plain_bitwise(D, b, dtype):
     rp_t = torch.from_numpy(rp).to(DEV)
     ci_t = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(DEV)
     a, la = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True)
-    per = -(-nq // 4)                                        # 4 segments per head
-    ws = torch.full((H * 4 * per,), -7, dtype=torch.int32, device=DEV)
+    nseg = 8 if b == 64 else 4                               # segments per head
+    per = -(-nq // nseg)
+    ws = torch.full((H * nseg * per,), -7, dtype=torch.int32, device=DEV)
+    assert S.balance_workspace_bytes(S.problem(Q, K, V, scale)) == ws.numel() * 4
     c, lc = S.sparstar_bsa_fwd_balanced(Q, K, V, rp_t, ci_t, scale, return_lse=True, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, c) and torch.equal(la, lc)
-    order = ws.cpu().numpy().reshape(H, 4, per)
+    order = ws.cpu().numpy().reshape(H, nseg, per)
     lens = np.diff(rp).reshape(H, nq)
     for h in range(H):
-        for x in range(4):
+        for x in range(nseg):
             seg = order[h, x]
             blocks = list(range(x * per, min((x + 1) * per, nq)))
             got = seg[:len(blocks)]
