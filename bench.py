@@ -239,11 +239,11 @@ def run_mass(args):
 
 
 def dispatch_order(B, H, n_q, block, xcds=8):
-    """Rows in the order bsa_fwd's workgroups are numbered: with S segments per head (8 at block
-    64, 4 otherwise) and per = ceil(n_q / S), workgroup w = 8 m + x runs query block
-    (x % S) * per + m % per of head (8 / S) (m // per) + x // S (a workgroup past n_q or past the
-    last head exits)."""
-    segments = 8 if block == 64 else 4
+    """Rows in the order bsa_fwd's workgroups are numbered: with S segments per head (4 at blocks
+    128 and 256 when B*H is even, else 8) and per = ceil(n_q / S), workgroup w = 8 m + x runs
+    query block (x % S) * per + m % per of head (8 / S) (m // per) + x // S (a workgroup past n_q
+    or past the last head exits)."""
+    segments = 4 if block != 64 and (B * H) % 2 == 0 else 8
     per = -(-n_q // segments)
     at_once = xcds // segments
     order = []

@@ -48,10 +48,10 @@
 // Workgroups are mapped to rows XCD-aware (with a row order for uneven lists,
 // each XCD starts the rows of its segment of a head longest list first).  Consecutive
 // workgroup ids are dispatched round-robin over the 8 XCDs.  A head's query blocks
-// are split into S contiguous segments of per = ceil(n_q / S) blocks, S = 4 at
-// b = 128 and 256: XCD x takes segment x % 4 of the even (x < 4) or odd (x >= 4)
-// head of each pair, pairs in order; S = 8 at b = 64: XCD x takes segment x of
-// every head.  The workgroups resident on one XCD are then consecutive query
+// are split into S contiguous segments of per = ceil(n_q / S) blocks.  S = 4 at
+// b = 128 and 256 with an even head count: XCD x takes segment x % 4 of the even
+// (x < 4) or odd (x >= 4) head of each pair, pairs in order; S = 8 at b = 64 or
+// with an odd head count: XCD x takes segment x of every head.  The workgroups resident on one XCD are then consecutive query
 // blocks of one head, whose block lists overlap and share that XCD's L2; and the
 // GPU works on one or two heads at a time, whose K and V fit the Infinity Cache,
 // so L2 misses are served there rather than by HBM.  (Which S is faster was
@@ -115,7 +115,7 @@ struct Shape {
 };
 
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
-__global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void attn_mfma_kernel(AttnArgs a, int per) {
+__global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void attn_mfma_kernel(AttnArgs a, int per, int seg_shift) {
   constexpr int BQ = Shape<kB>::BQ, BK = Shape<kB>::BK;
   constexpr int kThreads = Shape<kB>::kThreads, kWaves = Shape<kB>::kWaves;
   constexpr int kSubs = Shape<kB>::kSubs, kPasses = Shape<kB>::kPasses;
@@ -134,17 +134,16 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
   const Geometry& g = a.g;
   // Workgroup id -> (head, query block): XCD x = id % 8 takes the query blocks
   // [s * per, (s + 1) * per) of segment s = x % S of head (8 / S) j + x / S, with
-  // S = kSeg segments per head (8 / S heads at a time), heads in order.
+  // S = 1 << seg_shift segments per head (8 / S heads at a time), heads in order.
   // With a row order (uneven lists), the m-th workgroup of segment (head, s) runs the
   // segment's m-th longest row instead of its m-th.
-  constexpr int kSeg = segments_per_head(kB);
   const int64_t k = blockIdx.x / kXcds;
   const int64_t hset = k / per;
   const int xcd = (int)(blockIdx.x % kXcds), m = (int)(k - hset * per);
-  const int64_t bh = hset * (kXcds / kSeg) + xcd / kSeg;
+  const int64_t bh = (hset << (3 - seg_shift)) + (xcd >> seg_shift);
   if (bh >= (int64_t)g.B * g.H) return;  // uniform over the workgroup
-  const int seg = xcd % kSeg;
-  const int qi = a.row_order ? a.row_order[(bh * kSeg + seg) * per + m] : seg * per + m;
+  const int seg = xcd & ((1 << seg_shift) - 1);
+  const int qi = a.row_order ? a.row_order[((bh << seg_shift) + seg) * per + m] : seg * per + m;
   if (qi < 0 || qi >= g.n_q) return;  // uniform over the workgroup
   const int64_t row = bh * g.n_q + qi;
   const int bi = (int)(bh / g.H), hi = (int)(bh - (int64_t)bi * g.H);
@@ -550,13 +549,15 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
 
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  constexpr int kSeg = segments_per_head(kB);
-  constexpr int kHeadsAtOnce = kXcds / kSeg;
-  const int per = (a.g.n_q + kSeg - 1) / kSeg;
-  const int64_t grid = ((int64_t)a.g.B * a.g.H + kHeadsAtOnce - 1) / kHeadsAtOnce * per * kXcds;
+  const int64_t bh_count = (int64_t)a.g.B * a.g.H;
+  const int seg_count = segments_per_head(kB, bh_count);
+  const int seg_shift = seg_count == 8 ? 3 : 2;
+  const int heads_at_once = kXcds / seg_count;
+  const int per = (a.g.n_q + seg_count - 1) / seg_count;
+  const int64_t grid = (bh_count + heads_at_once - 1) / heads_at_once * per * kXcds;
   if (grid > 0xffffffffll) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_mfma_kernel<kB, kDense, kOutBf16, kLse>), dim3((unsigned)grid),
-                     dim3(Shape<kB>::kThreads), 0, s, a, per);
+                     dim3(Shape<kB>::kThreads), 0, s, a, per, seg_shift);
   return hipSuccess;
 }
 

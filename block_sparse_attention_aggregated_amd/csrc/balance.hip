@@ -4,7 +4,7 @@
 // SpaceTime AutoRegressive Video Synthesis", section 5 "Forward-Only Sparse
 // Execution") runs one workgroup per query-block row.  Its workgroups are
 // numbered so that a head's query blocks form S contiguous segments
-// [x * per, (x + 1) * per) (per = ceil(n_q / S), S = segments_per_head(b)), each
+// [x * per, (x + 1) * per) (per = ceil(n_q / S), S = segments_per_head(b, B*H)), each
 // run by one XCD, heads in order: the rows in flight belong to one or two heads,
 // whose K and V stay in the Infinity Cache.  With uneven lists the rows handed
 // out last set the tail: a long row started last keeps part of the GPU busy
@@ -59,14 +59,14 @@ __global__ __launch_bounds__(kThreads) void row_order_kernel(const int32_t* row_
 }  // namespace
 
 int64_t row_order_entries(int64_t bh, int32_t n_q, int32_t b) {
-  const int S = segments_per_head(b);
+  const int S = segments_per_head(b, bh);
   return bh * S * (int64_t)((n_q + S - 1) / S);
 }
 
 hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int32_t b, int64_t col_idx_len,
                             int32_t* order, hipStream_t s) {
   if (bh == 0 || n_q == 0) return hipSuccess;
-  const int32_t S = segments_per_head(b);
+  const int32_t S = segments_per_head(b, bh);
   const int32_t per = (n_q + S - 1) / S;
   const int64_t segs = bh * S;
   if (segs > 0xffffffffll || (size_t)per * sizeof(int32_t) > 64 * 1024) return hipErrorInvalidValue;

@@ -107,10 +107,12 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // Attention row mapping: the query blocks of a head are split into S contiguous
 // segments of per = ceil(n_q / S) blocks; workgroup id w runs on XCD
 // x = w % kXcds, which takes segment x % S of head (w / kXcds / per) * (kXcds / S)
-// + x / S, so kXcds / S heads are in flight at a time, each on S XCDs.  S = 8 at
-// b = 64 and 4 otherwise (measured: each is the faster one at its block size).
+// + x / S, so kXcds / S heads are in flight at a time, each on S XCDs.  S = 4 at
+// b = 128 and 256 when the number of heads B*H is even, else 8 (measured: four is
+// faster at b = 128 and 256, eight at b = 64; with an odd head count the last head
+// would leave half the XCDs idle).
 constexpr int kXcds = 8;
-constexpr int segments_per_head(int b) { return b == 64 ? 8 : 4; }
+constexpr int segments_per_head(int b, int64_t bh) { return (b != 64 && bh % 2 == 0) ? 4 : 8; }
 // Query blocks of each (head, segment) ordered by list length, longest first:
 // order[(bh * S + x) * ceil(n_q / S) + m], -1 past a segment's end.
 int64_t row_order_entries(int64_t bh, int32_t n_q, int32_t b);

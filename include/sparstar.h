@@ -171,15 +171,15 @@ sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const v
                                const void* v, void* out, float* lse, void* stream);
 
 /* Bytes of device workspace sparstar_bsa_fwd_balanced needs: 4 * B*H*S*ceil(n_q/S),
- * with S = 8 segments per head at block 64 and 4 at blocks 128 and 256;
- * -1 if the problem is invalid. */
+ * with S = 4 segments per head at blocks 128 and 256 when B*H is even, and S = 8
+ * otherwise; -1 if the problem is invalid. */
 int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p);
 
 /* sparstar_bsa_fwd for block lists of uneven length (section 5 "Forward-Only Sparse
  * Execution": the lists are per query block and their lengths are the caller's).
  * The attention runs the query blocks of a head in S contiguous segments of
- * ceil(n_q/S) blocks, one per XCD (S = 8 at block 64: one head at a time; S = 4 at
- * blocks 128 and 256: two heads at a time), heads in order; here the rows of each
+ * ceil(n_q/S) blocks, one per XCD (S = 4 at blocks 128 and 256 with an even B*H: two
+ * heads at a time; S = 8 otherwise: one head at a time), heads in order; here the rows of each
  * segment are first ordered by list length, longest first and stably (equal lengths
  * keep their order), into `workspace` (a device buffer of at least
  * sparstar_balance_workspace_bytes, owned by the caller; on return it holds the

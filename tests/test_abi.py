@@ -185,6 +185,9 @@ def test_mass_entry_points_validate_before_any_device_call():
     assert L.sparstar_balance_workspace_bytes(ctypes.byref(p64)) == 16 * 8 * 10 * 4
     p256 = _prob(I.S192P_B256)                                                   # n_q = 20: 4 segments of 5
     assert L.sparstar_balance_workspace_bytes(ctypes.byref(p256)) == 16 * 4 * 5 * 4
+    p.heads = 15                                                                 # odd head count: 8 segments of 5
+    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p)) == 15 * 8 * 5 * 4
+    p.heads = 16
     assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, 10, b, None, None, 1 << 20, None) \
         == S.ERR_NULL
     assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, 10, b, None, b, 16 * 40 * 4 - 1, None) \

@@ -48,12 +48,14 @@ def test_uneven_lists_recipe():
     assert 1 <= counts.min() and counts.max() <= 19
     _, _, even = bench.uneven_lists(50, 40, 3, 10, seed=1, even=True)
     assert np.all(even == 10)
-    for B, H, n_q, block in ((1, 2, 11, 128), (2, 3, 13, 64), (1, 5, 563, 128), (1, 1, 1, 256)):
+    for B, H, n_q, block in ((1, 2, 11, 128), (2, 3, 13, 64), (1, 5, 563, 128), (1, 1, 1, 256), (3, 1, 9, 128)):
         order = bench.dispatch_order(B, H, n_q, block)
         assert sorted(order.tolist()) == list(range(B * H * n_q))
     # b = 128: XCDs 0-3 split the even head into 4 segments, XCDs 4-7 the odd one
     order = bench.dispatch_order(1, 2, 11, 128)
     assert order[:8].tolist() == [0, 3, 6, 9, 11 + 0, 11 + 3, 11 + 6, 11 + 9]
-    # b = 64: 8 segments, one head at a time
+    # b = 64, or an odd head count: 8 segments, one head at a time
     order = bench.dispatch_order(1, 2, 16, 64)
+    assert order[:8].tolist() == [0, 2, 4, 6, 8, 10, 12, 14]
+    order = bench.dispatch_order(1, 3, 16, 128)
     assert order[:8].tolist() == [0, 2, 4, 6, 8, 10, 12, 14]

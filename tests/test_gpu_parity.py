@@ -334,13 +334,15 @@ def test_irregular_csr(D, b, dtype):
             assert np.max(np.abs(got_l[s:e] - l_ref)) < LSE_BF16
 
 
-@pytest.mark.parametrize("D,b,dtype", [(128, 128, torch.bfloat16), (128, 64, torch.bfloat16),
-                                       (128, 256, torch.bfloat16), (64, 64, torch.float32)])
-def test_balanced_equals_plain_bitwise(D, b, dtype):
+@pytest.mark.parametrize("D,b,dtype,H", [(128, 128, torch.bfloat16, 3), (128, 64, torch.bfloat16, 3),
+                                         (128, 256, torch.bfloat16, 3), (64, 64, torch.float32, 3),
+                                         (128, 128, torch.bfloat16, 2), (128, 256, torch.bfloat16, 4)])
+def test_balanced_equals_plain_bitwise(D, b, dtype, H):
     """Rows started longest list first give the same outputs, bit for bit, as the plain call:
-    uneven random lists plus the irregular kinds (empty, duplicates, out of range)."""
-    L_text, L_ref, L_q, H = 64, 900, 1000, 3
-    print_case("balanced", D, b, dtype)
+    uneven random lists plus the irregular kinds (empty, duplicates, out of range); odd head
+    counts use 8 segments per head, even ones at b = 128 and 256 use 4."""
+    L_text, L_ref, L_q = 64, 900, 1000
+    print_case("balanced", D, b, dtype, H)
     Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, D, dtype, seed=12)
     scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(D))
     nq, nk = O.num_blocks(L_q, b), O.num_blocks(L_text + L_ref + L_q, b)
@@ -358,7 +360,7 @@ def test_balanced_equals_plain_bitwise(D, b, dtype):
     rp_t = torch.from_numpy(rp).to(DEV)
     ci_t = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(DEV)
     a, la = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True)
-    nseg = 8 if b == 64 else 4                               # segments per head
+    nseg = 4 if b != 64 and H % 2 == 0 else 8               # segments per head
     per = -(-nq // nseg)
     ws = torch.full((H * nseg * per,), -7, dtype=torch.int32, device=DEV)
     assert S.balance_workspace_bytes(S.problem(Q, K, V, scale)) == ws.numel() * 4
