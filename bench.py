@@ -71,6 +71,9 @@ def parse():
                     help="run the attention through sparstar_bsa_fwd_balanced (rows started longest list first)")
     ap.add_argument("--longest-first", action="store_true",
                     help="with --uneven: give the longest lists to the rows the kernel dispatches first")
+    ap.add_argument("--fused-select", action="store_true",
+                    help="score and select in one kernel (sparstar_pool_blocks + sparstar_score_select) "
+                         "instead of sparstar_pool_score + sparstar_select_blocks")
     ap.add_argument("--mass", action="store_true",
                     help="retained attention mass of the selection strategies instead (times block_mass)")
     ap.add_argument("--mass-queries", type=int, default=512,
@@ -339,10 +342,16 @@ def main():
                     events[n][2].record(stream)
                 S.dense_attn_fwd(s["Q"], s["K"], s["V"], s["sc"], out=s["out"])
             else:
-                S.sparstar_pool_score(s["Q"], s["K"], s["sc"], s["qp"], s["kp"], s["scores"])
+                if args.fused_select:
+                    S.sparstar_pool_blocks(s["Q"], s["K"], s["sc"], s["qp"], s["kp"])
+                else:
+                    S.sparstar_pool_score(s["Q"], s["K"], s["sc"], s["qp"], s["kp"], s["scores"])
                 if events is not None:
                     events[n][1].record(stream)
-                if not args.uneven:
+                if args.fused_select and not args.uneven:
+                    S.sparstar_score_select(s["qp"], s["kp"], s["Q"], s["K"], s["sc"], s["density"], s["policy"],
+                                            row_ptr=s["rp"], col_idx=s["ci"])
+                elif not args.uneven:
                     S.sparstar_select_blocks(s["scores"], s["Q"], s["K"], s["sc"], s["density"], s["policy"],
                                              row_ptr=s["rp"], col_idx=s["ci"])
                 if events is not None:
@@ -382,7 +391,8 @@ def main():
             "ms_scale": float(tot.mean()),
             "exec_tflop": s["flops"] / 1e12,
             "attention_tflops": s["flops"] / (att.mean() * 1e-3) / 1e12,
-            "scoring_gbs": (scoring_bytes(cfg) / (pool.mean() * 1e-3) / 1e9) if not args.dense else None,
+            "scoring_gbs": ((scoring_bytes(cfg) / (pool.mean() * 1e-3) / 1e9)
+                            if not args.dense and not args.fused_select else None),
         })
     flops = sum(s["flops"] for s in scales)
     ms_step = wall * 1e3 / args.steps      # bracketed by device synchronisation
@@ -412,7 +422,8 @@ def main():
             "density": scales[0]["density"] if len(scales) == 1 else [s["density"] for s in scales],
             "mode": ("dense" if args.dense else (("sparse, random lists of equal length" if args.random_even else
                                                   "sparse, uneven random lists") if args.uneven else "sparse"))
-                    + (", balanced (longest list first)" if args.balanced else ""),
+                    + (", balanced (longest list first)" if args.balanced else "")
+                    + (", fused score-then-select" if args.fused_select else ""),
             "out_dtype": str(scales[0]["out"].dtype).replace("torch.", ""),
             "parallelism": "single GPU",
         },
@@ -428,7 +439,7 @@ def main():
                         and not args.dense and not args.uneven else None),
         },
     }
-    if not args.dense and len(scales) == 1:
+    if not args.dense and not args.fused_select and len(scales) == 1:
         p = per_scale[0]
         rec["scoring_roofline"] = {"kernel": "sparstar_pool_score", "bound": "hbm",
                                    "achieved": p["scoring_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",

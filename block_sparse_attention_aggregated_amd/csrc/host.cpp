@@ -325,6 +325,73 @@ sparstar_status sparstar_select_blocks(const sparstar_problem* p, const float* s
   });
 }
 
+sparstar_status sparstar_pool_blocks(const sparstar_problem* p, const void* q, const void* k, float* q_pool,
+                                     float* k_pool, void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar_status s = check_problem_impl(p);
+    if (s != SPARSTAR_OK) return s;
+    if (!q || !k || !q_pool || !k_pool) return fail(SPARSTAR_ERR_NULL, "q, k, q_pool and k_pool must be non-NULL");
+    if (!is_aligned16(q) || !is_aligned16(k) || !is_aligned16(q_pool) || !is_aligned16(k_pool))
+      return fail(SPARSTAR_ERR_LAYOUT, "q, k, q_pool and k_pool must be 16-byte aligned");
+    sparstar::PoolScoreArgs a;
+    a.g = geometry(p);
+    if ((int64_t)a.g.B * a.g.H == 0) return ok();
+    a.dtype = p->dtype;
+    a.q = q;
+    a.k = k;
+    a.qs_b = p->q_stride[0]; a.qs_h = p->q_stride[1]; a.qs_t = p->q_stride[2];
+    a.ks_b = p->k_stride[0]; a.ks_h = p->k_stride[1]; a.ks_t = p->k_stride[2];
+    a.q_pool = q_pool;
+    a.k_pool = k_pool;
+    a.scores = nullptr;
+    a.sigma = p->softmax_scale;
+    if ((s = check_device()) != SPARSTAR_OK) return s;
+    return launched(sparstar::launch_pool_score(a, (hipStream_t)stream), "pool_blocks launch");
+  });
+}
+
+sparstar_status sparstar_score_select(const sparstar_problem* p, const float* q_pool, const float* k_pool,
+                                      double density, int32_t policy, int32_t* row_ptr, int32_t* col_idx,
+                                      int64_t col_idx_capacity, void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar_status s = check_problem_impl(p);
+    if (s != SPARSTAR_OK) return s;
+    if (!(density > 0.0 && density <= 1.0))
+      return fail(SPARSTAR_ERR_DENSITY, "density %g not in (0, 1]", density);
+    if (policy != SPARSTAR_POLICY_LATER_CLIP && policy != SPARSTAR_POLICY_FIRST_CLIP)
+      return fail(SPARSTAR_ERR_UNSUPPORTED, "policy %d not built", policy);
+    if (!q_pool || !k_pool || !row_ptr || !col_idx)
+      return fail(SPARSTAR_ERR_NULL, "q_pool, k_pool, row_ptr and col_idx must be non-NULL");
+    if (!is_aligned16(q_pool) || !is_aligned16(k_pool) || (reinterpret_cast<uintptr_t>(row_ptr) & 3u) ||
+        (reinterpret_cast<uintptr_t>(col_idx) & 3u))
+      return fail(SPARSTAR_ERR_LAYOUT, "q_pool and k_pool must be 16-byte aligned, row_ptr/col_idx 4-byte aligned");
+    const sparstar::Geometry g = geometry(p);
+    const int64_t keep = std::min<int64_t>(num_retained(p, policy), g.n_k);
+    const int64_t n_cand = g.n_k - keep;
+    const int64_t kk = budget_impl(n_cand, density);
+    const int64_t rows = (int64_t)g.B * g.H * g.n_q;
+    const int64_t nnz = rows * (keep + kk);
+    if (nnz > (int64_t)INT32_MAX) return fail(SPARSTAR_ERR_SHAPE, "nnz %lld exceeds int32", (long long)nnz);
+    if (col_idx_capacity < nnz)
+      return fail(SPARSTAR_ERR_CAPACITY, "col_idx capacity %lld < nnz %lld", (long long)col_idx_capacity,
+                  (long long)nnz);
+    if (g.n_k > sparstar::score_select_max_keys())
+      return fail(SPARSTAR_ERR_UNSUPPORTED, "%d key blocks; the fused kernel holds at most %d (use pool_score "
+                  "and select_blocks)", g.n_k, sparstar::score_select_max_keys());
+    if ((s = check_device()) != SPARSTAR_OK) return s;
+    sparstar::ScoreSelectArgs a;
+    a.g = g;
+    a.q_pool = q_pool;
+    a.k_pool = k_pool;
+    a.sigma = p->softmax_scale;
+    a.n_keep = (int32_t)keep;
+    a.k = (int32_t)kk;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    return launched(sparstar::launch_score_select(a, (hipStream_t)stream), "score_select launch");
+  });
+}
+
 sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const void* k, const void* v,
                                  const int32_t* row_ptr, const int32_t* col_idx, int64_t col_idx_len,
                                  void* out, float* lse, void* stream) {

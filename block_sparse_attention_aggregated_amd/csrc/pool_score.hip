@@ -239,6 +239,7 @@ hipError_t launch_pool_score(const PoolScoreArgs& a, hipStream_t s) {
   else
     e = a.g.D == 128 ? launch_pool<float, 128>(a, s) : launch_pool<float, 64>(a, s);
   if (e != hipSuccess) return e;
+  if (a.scores == nullptr) return hipSuccess;  // pooling only
   const int ti = (a.g.n_q + kTileI - 1) / kTileI, tj = (a.g.n_k + kTileJ - 1) / kTileJ;
   // XCD-aware grid: ceil(B*H / 8) head groups of 8, one per XCD lane of the id.
   const int64_t tiles = ((int64_t)a.g.B * a.g.H + kXcds - 1) / kXcds * kXcds * ti * tj;

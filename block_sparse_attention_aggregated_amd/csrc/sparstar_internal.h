@@ -23,8 +23,20 @@ struct PoolScoreArgs {
   int64_t ks_b, ks_h, ks_t;
   float* q_pool;             // [B,H,n_q,D]
   float* k_pool;             // [B,H,n_k,D]
-  float* scores;             // [B,H,n_q,n_k]
+  float* scores;             // [B,H,n_q,n_k]; nullptr: pooling only
   float sigma;
+};
+
+// Scores and selection in one kernel (no score matrix in memory).
+struct ScoreSelectArgs {
+  Geometry g;
+  const float* q_pool;       // [B,H,n_q,D] contiguous
+  const float* k_pool;       // [B,H,n_k,D] contiguous
+  float sigma;
+  int32_t n_keep;            // retained prefix [0, n_keep)
+  int32_t k;                 // candidates taken per row
+  int32_t* row_ptr;          // [B*H*n_q + 1]
+  int32_t* col_idx;
 };
 
 struct SelectArgs {
@@ -104,6 +116,11 @@ hipError_t launch_selection_mass(const SelMassArgs& a, hipStream_t s);
 hipError_t launch_window_scores(float* out, int64_t bh, int n_q, int n_k, int b, int64_t offset, hipStream_t s);
 hipError_t launch_token_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// row_ptr[r] = r * per_row for r = 0 .. rows.
+hipError_t launch_row_ptr(int32_t* row_ptr, int64_t rows, int32_t per_row, hipStream_t s);
+// Largest n_k the fused score-and-select kernel holds (a strip's keys in LDS).
+int score_select_max_keys();
+hipError_t launch_score_select(const ScoreSelectArgs& a, hipStream_t s);
 // Attention row mapping: the query blocks of a head are split into S contiguous
 // segments of per = ceil(n_q / S) blocks; workgroup id w runs on XCD
 // x = w % kXcds, which takes segment x % S of head (w / kXcds / per) * (kXcds / S)

@@ -60,6 +60,9 @@ _SIGS = {
     "sparstar_pool_score": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "sparstar_select_blocks": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_dbl, _c_i32, _c_vp, _c_vp,
                                         _c_i64, _c_vp]),
+    "sparstar_pool_blocks": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "sparstar_score_select": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_dbl, _c_i32, _c_vp, _c_vp,
+                                       _c_i64, _c_vp]),
     "sparstar_bsa_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
                                   _c_vp, _c_vp, _c_vp]),
     "dense_attn_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
@@ -237,6 +240,48 @@ def sparstar_select_blocks(scores: torch.Tensor, q: torch.Tensor, k: torch.Tenso
         col_idx = torch.empty((max(nnz, 1),), dtype=torch.int32, device=dev)
     _check(lib().sparstar_select_blocks(ctypes.byref(p), _ptr(scores), float(density), policy,
                                         _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(dev)))
+    return row_ptr, col_idx[:nnz]
+
+
+def sparstar_pool_blocks(q: torch.Tensor, k: torch.Tensor, scale: Scale, q_pool=None,
+                         k_pool=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block means of Q and K (float32), without the scores."""
+    p = problem(q, k, None, scale)
+    B, H, _, D = q.shape
+    nq, nk = num_q_blocks(p), num_k_blocks(p)
+    dev = q.device
+    if q_pool is None:
+        q_pool = torch.empty((B, H, nq, D), dtype=torch.float32, device=dev)
+    if k_pool is None:
+        k_pool = torch.empty((B, H, nk, D), dtype=torch.float32, device=dev)
+    for t, shape in ((q_pool, (B, H, nq, D)), (k_pool, (B, H, nk, D))):
+        if tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != torch.float32:
+            raise SparstarError(ERR_SHAPE, f"expected contiguous float32 {shape}, got {tuple(t.shape)}")
+    _check(lib().sparstar_pool_blocks(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(q_pool), _ptr(k_pool),
+                                      _stream(dev)))
+    return q_pool, k_pool
+
+
+def sparstar_score_select(q_pool: torch.Tensor, k_pool: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                          scale: Scale, density: float, policy: int = POLICY_LATER_CLIP, row_ptr=None,
+                          col_idx=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """CSR block lists from the block means, scores formed on chip (no score matrix)."""
+    p = problem(q, k, None, scale)
+    B, H, _, D = q.shape
+    nq, nk = num_q_blocks(p), num_k_blocks(p)
+    for t, shape in ((q_pool, (B, H, nq, D)), (k_pool, (B, H, nk, D))):
+        if tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != torch.float32:
+            raise SparstarError(ERR_SHAPE, f"expected contiguous float32 {shape}, got {tuple(t.shape)}")
+    nnz = select_nnz(p, density, policy)
+    if nnz < 0:
+        raise SparstarError(ERR_DENSITY, f"density {density} / policy {policy} rejected")
+    dev = q_pool.device
+    if row_ptr is None:
+        row_ptr = torch.empty((B * H * nq + 1,), dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty((max(nnz, 1),), dtype=torch.int32, device=dev)
+    _check(lib().sparstar_score_select(ctypes.byref(p), _ptr(q_pool), _ptr(k_pool), float(density), policy,
+                                       _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(dev)))
     return row_ptr, col_idx[:nnz]
 
 

@@ -128,6 +128,27 @@ const char* sparstar_last_error(void);
 sparstar_status sparstar_pool_score(const sparstar_problem* p, const void* q, const void* k,
                                     float* q_pool, float* k_pool, float* scores, void* stream);
 
+/* Step 2 without the scores: the block means of sparstar_pool_score only (same
+ * arguments and results for q_pool and k_pool, bit for bit), for
+ * sparstar_score_select. */
+sparstar_status sparstar_pool_blocks(const sparstar_problem* p, const void* q, const void* k,
+                                     float* q_pool, float* k_pool, void* stream);
+
+/* Steps 2b and 3 fused (section 5 "Per-head aggregated query-key score" and
+ * "Clip-Dependent Retained and Selectable Blocks"; the scope's "score-then-select
+ * that never materialises S"): the block lists of sparstar_select_blocks computed
+ * from the block means, with no score matrix in memory.  For each head and strip
+ * of 32 query blocks the scores are formed in LDS, in the same float32 operations
+ * as sparstar_pool_score, so row_ptr and col_idx are the same, bit for bit, as
+ * sparstar_pool_score followed by sparstar_select_blocks.
+ *   q_pool, k_pool : in, float32 [B, H, n_q, D] / [B, H, n_k, D] contiguous
+ *                    (sparstar_pool_blocks or sparstar_pool_score).
+ *   density, policy, row_ptr, col_idx, col_idx_capacity : as sparstar_select_blocks.
+ * A strip's scores must fit LDS: n_k at most 1,216 (SPARSTAR_ERR_UNSUPPORTED beyond). */
+sparstar_status sparstar_score_select(const sparstar_problem* p, const float* q_pool, const float* k_pool,
+                                      double density, int32_t policy, int32_t* row_ptr, int32_t* col_idx,
+                                      int64_t col_idx_capacity, void* stream);
+
 /* Step 3 (section 5 "Clip-Dependent Retained and Selectable Blocks" and
  * "Forward-Only Sparse Execution"; appendix A.7).  For every row
  * r = (b*H + h)*n_q + i the listed blocks are the retained prefix [0, r_keep)

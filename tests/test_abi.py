@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 19
+    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 21
+    assert {"sparstar_pool_blocks", "sparstar_score_select"} <= set(names)
     assert {"sparstar_block_mass", "sparstar_selection_mass", "sparstar_window_scores",
             "sparstar_token_topk_mass"} <= set(names)
     L = ctypes.CDLL(S.LIB_PATH)
@@ -159,6 +160,28 @@ def test_null_and_alignment_and_density_and_capacity():
     assert st == S.ERR_CAPACITY and "capacity" in S.last_error()
     assert L.sparstar_select_blocks(ctypes.byref(p), b, 0.3, 0, None, b, nnz, None) == S.ERR_NULL
     assert S.status_string(S.ERR_CAPACITY) == "output capacity too small"
+
+
+@no_gpu
+def test_fused_select_entry_points_validate_before_any_device_call():
+    p = _prob(I.S192P)
+    L = S.lib()
+    b = ctypes.c_void_p(BOGUS)
+    odd = ctypes.c_void_p(BOGUS + 4)
+    nnz = S.select_nnz(p, 0.3)
+    assert L.sparstar_pool_blocks(None, b, b, b, b, None) == S.ERR_NULL
+    assert L.sparstar_pool_blocks(ctypes.byref(p), b, b, None, b, None) == S.ERR_NULL
+    assert L.sparstar_pool_blocks(ctypes.byref(p), b, b, odd, b, None) == S.ERR_LAYOUT
+    for rho in (0.0, 1.5, float("nan")):
+        assert L.sparstar_score_select(ctypes.byref(p), b, b, rho, 0, b, b, nnz, None) == S.ERR_DENSITY
+    assert L.sparstar_score_select(ctypes.byref(p), b, b, 0.3, 7, b, b, nnz, None) == S.ERR_UNSUPPORTED
+    assert L.sparstar_score_select(ctypes.byref(p), None, b, 0.3, 0, b, b, nnz, None) == S.ERR_NULL
+    assert L.sparstar_score_select(ctypes.byref(p), odd, b, 0.3, 0, b, b, nnz, None) == S.ERR_LAYOUT
+    assert L.sparstar_score_select(ctypes.byref(p), b, b, 0.3, 0, b, b, nnz - 1, None) == S.ERR_CAPACITY
+    # a strip's scores must fit LDS: 1,216 key blocks at most
+    big = _prob(I.S720P.with_(block=64))                                        # n_k = 2,258
+    st = L.sparstar_score_select(ctypes.byref(big), b, b, 0.2, 0, b, b, 10**9, None)
+    assert st == S.ERR_UNSUPPORTED and "1216" in S.last_error()
 
 
 @no_gpu

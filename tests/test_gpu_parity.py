@@ -582,6 +582,49 @@ def test_random_shapes_end_to_end(case):
             assert np.max(np.abs(got_l[s:e] - l_ref)) < LSE_BF16, (h, i)
 
 
+# ---------------------------------------------------------------- fused score-then-select
+
+def _fused_equals_unfused(Q, K, sc, rho, policy):
+    qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, rho, policy)
+    qp2, kp2 = S.sparstar_pool_blocks(Q, K, sc)
+    rp2, ci2 = S.sparstar_score_select(qp2, kp2, Q, K, sc, rho, policy)
+    torch.cuda.synchronize()
+    assert torch.equal(qp, qp2) and torch.equal(kp, kp2)
+    assert torch.equal(rp, rp2)
+    assert torch.equal(ci, ci2), int((ci != ci2).sum())
+
+
+@pytest.mark.parametrize("name,rho", [("tiny_f32", 0.5), ("tiny_f32", 1.0), ("192p", 0.3), ("192p_b64", 0.3),
+                                      ("192p_b256", 0.3), ("tiny_f32_b256", 0.5), ("480p", 0.25),
+                                      ("720p_clip1_s1", None), ("480p_clip2_s3", None), ("720p", 0.2)])
+def test_fused_score_select_equals_unfused_bitwise(name, rho):
+    """The fused kernel forms each score with the score kernel's float32 operations and ranks
+    with the same row selector: pooled blocks and block lists equal the unfused path's bit for
+    bit (the unfused path is checked against the oracle elsewhere)."""
+    cfg = I.WORKLOADS[name]
+    rho = cfg.densities[0] if rho is None else rho
+    print_case("fused select", cfg.name, rho, cfg.policy)
+    Q, K, V = inputs(cfg)
+    _fused_equals_unfused(Q, K, scale_of(cfg), rho, cfg.policy)
+
+
+def test_fused_score_select_random_shapes():
+    """The seeded random problems of the end-to-end test whose key blocks fit the fused kernel:
+    equal to the unfused path bit for bit (partial strips, both policies, D = 64 and 128)."""
+    n = 0
+    for c in _random_cases():
+        n_k = O.num_blocks(c["L_text"] + c["L_ref"] + c["L_q"], c["b"])
+        if n_k > 1216:
+            continue
+        print_case("fused select random", c)
+        Q, K, V = _custom_inputs(c["L_text"], c["L_ref"], c["L_q"], c["H"], c["D"], c["dtype"], seed=c["seed"])
+        sc = S.Scale(c["L_text"], c["L_ref"], c["b"], 1 / math.sqrt(c["D"]))
+        _fused_equals_unfused(Q, K, sc, c["rho"], c["policy"])
+        n += 1
+    assert n >= 8
+
+
 # ---------------------------------------------------------------- graph capture
 
 def test_step_captured_in_a_graph_replays_exactly():
