@@ -22,7 +22,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_help_lists_the_modes():
     r = _run("--help")
     assert r.returncode == 0
-    for opt in ("--workload", "--density", "--dense", "--mass", "--uneven", "--balanced", "--no-cpu-baseline",
+    for opt in ("--workload", "--density", "--dense", "--mass", "--uneven", "--balanced", "--fused-select", "--no-cpu-baseline",
                 "--steps", "--warmup"):
         assert opt in r.stdout, opt
 
