@@ -236,6 +236,16 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
   // LDS read offsets.  K: row kt*32 + l32, logical chunk 2ks + hl, physical chunk
   // (2ks + hl) ^ (row & 15) = 2ks ^ (hl ^ (l32 & 15)); kt adds 32 rows.
   const uint32_t k_row = l32 * (HD * 2), k_sw = hl ^ (l32 & 15);
+  // The lane's offset for each feature step stays in a register for the whole
+  // launch (the empty asm keeps the compiler from re-forming it with an add at
+  // every read), so each K read is one ds_read_b128 with the buffer and the key
+  // tile in its immediate offset.
+  uint32_t kr_off[HD / 16];
+#pragma unroll
+  for (int ks = 0; ks < HD / 16; ++ks) {
+    kr_off[ks] = k_row + (((2 * ks) ^ k_sw) << 4);
+    asm volatile("" : "+v"(kr_off[ks]));
+  }
   // V^T operand by transposing reads.  Lane L = 16g + m points at key
   // 16ks + 8r + 4(g >> 1) + (m >> 2) (r = 0, 1 for the two reads of a step) and
   // features 32dt + 16(g & 1) + 4(m & 3) .. +4: chunk 4dt + cc, cc = 2(g & 1) + (m & 3) / 2,
@@ -290,7 +300,7 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
   auto load_v = [&](const Sub& s, lds_char* buf) { load_tile(vbase, vs_b, v_off, s, buf); };
   auto k_frag = [&](lds_char* buf, int kt, int ks) -> bf16x8 {
     typedef const __attribute__((address_space(3))) bf16x8* lds_bf16x8;
-    return *(lds_bf16x8)(buf + kt * 32 * (HD * 2) + k_row + (((2 * ks) ^ k_sw) << 4));
+    return *(lds_bf16x8)(buf + kt * 32 * (HD * 2) + kr_off[ks]);
   };
   auto v_frag = [&](lds_char* buf, int dt, int ks) -> bf16x8 {
     typedef __attribute__((address_space(3))) v4s* lds_v4s;
