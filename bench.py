@@ -76,8 +76,11 @@ def parse():
                          "instead of sparstar_pool_score + sparstar_select_blocks")
     ap.add_argument("--mass", action="store_true",
                     help="retained attention mass of the selection strategies instead (times block_mass)")
-    ap.add_argument("--mass-queries", type=int, default=512,
-                    help="sampled queries for the token-wise Top-K bound in --mass mode")
+    ap.add_argument("--mass-blocks", type=int, default=32,
+                    help="seeded sampled query blocks (all their real queries) on which --mass compares the "
+                         "token-wise Top-K bound with the block selections")
+    ap.add_argument("--no-report", action="store_true",
+                    help="skip the per-configuration report (192p, 480p, 720p at 0.1/0.2/0.4/1.0, sweep)")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -160,6 +163,7 @@ def cpu_baseline(cfg, density, policy, Q, K, V, rows_per_head):
     t_total = t_sel + t_att * flops_all / max(flops_rows, 1)
     return {
         "value": flops_all / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(), "host_cpus_available": len(os.sched_getaffinity(0)),
         "ms_per_scale_extrapolated": t_total * 1e3,
         "sample": (f"float64 numpy oracle on the same inputs: pooling+scoring+selection of all "
                    f"{cfg.batch * cfg.heads} heads ({t_sel:.1f} s) and attention of {n_rows} of "
@@ -205,19 +209,34 @@ def run_mass(args):
     rnd = torch.rand(mass.shape, generator=gen, device=dev, dtype=torch.float32)
     _, _, scores = S.sparstar_pool_score(Q, K, sc)
     window = S.sparstar_window_scores(Q, K, sc)
-    res = {}
+    res, row_mass = {}, {}
     for name, src in (("block_oracle", mass), ("aggregated_qk", scores), ("window", window), ("random", rnd)):
         rp, ci = S.sparstar_select_blocks(src, Q, K, sc, density, cfg.policy)
-        res[name] = float(S.sparstar_selection_mass(mass, rp, ci, Q, K, sc).mean())
+        row_mass[name] = S.sparstar_selection_mass(mass, rp, ci, Q, K, sc).cpu().numpy().astype(np.float64)
+        res[name] = float(row_mass[name].mean())
+    # matched queries: every real query of seeded sampled query blocks gets the token-wise bound; the
+    # selections' masses are read for the same blocks (each a mean over the same real queries)
     p = S.problem(Q, K, None, sc)
     r = S.num_retained(p, cfg.policy)
     kk = S.blocks_per_row(p, density, cfg.policy) - r
-    g = torch.Generator(device=dev).manual_seed(99)
-    rows = torch.randint(0, cfg.batch * cfg.heads * cfg.len_q, (args.mass_queries,), generator=g, device=dev)
-    tok = S.sparstar_token_topk_mass(Q, K, lse, rows, r * cfg.block, kk * cfg.block, sc)
-    # the same queries under the block oracle's blocks, for the gap at matched queries
+    nq = S.num_q_blocks(p)
+    n_rows = cfg.batch * cfg.heads * nq
+    rng = np.random.default_rng(99)
+    sample = np.sort(rng.choice(n_rows, min(args.mass_blocks, n_rows), replace=False))
+    q_index, q_block = [], []
+    for n, row in enumerate(sample):
+        bh, i = divmod(int(row), nq)
+        for t in range(i * cfg.block, min((i + 1) * cfg.block, cfg.len_q)):
+            q_index.append(bh * cfg.len_q + t)
+            q_block.append(n)
+    rows = torch.tensor(q_index, dtype=torch.int64, device=dev)
+    tok = S.sparstar_token_topk_mass(Q, K, lse, rows, r * cfg.block, kk * cfg.block, sc).cpu().numpy()
+    q_block = np.array(q_block)
+    tok_rows = np.bincount(q_block, weights=tok) / np.bincount(q_block)
+    sampled = {"token_topk_bound": float(tok_rows.mean())}
+    for name in ("block_oracle", "aggregated_qk", "window", "random"):
+        sampled[name] = float(row_mass[name][sample].mean())
     torch.cuda.synchronize()
-    res["token_topk_bound_sampled"] = float(tok.mean())
     rec = {
         "metric": "retained attention mass (mean over query blocks) and block-mass pass time",
         "value": res["aggregated_qk"], "unit": "fraction of dense softmax mass", "n_gpus": 1,
@@ -225,10 +244,13 @@ def run_mass(args):
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "heads": cfg.heads, "density": density, "block": cfg.block,
                    "policy": "first clip" if cfg.policy == 1 else "later clip",
-                   "token_bound_queries": args.mass_queries},
+                   "sampled_query_blocks": len(sample), "sampled_queries": len(q_index)},
         "retained_mass": res,
-        "gaps": {"blockization (token bound - block oracle)": res["token_topk_bound_sampled"] - res["block_oracle"],
-                 "scoring (block oracle - aggregated QK)": res["block_oracle"] - res["aggregated_qk"]},
+        "retained_mass_sampled_blocks": sampled,
+        "gaps_matched": {
+            "blockization (token bound - block oracle)": sampled["token_topk_bound"] - sampled["block_oracle"],
+            "scoring (block oracle - aggregated QK)": sampled["block_oracle"] - sampled["aggregated_qk"],
+            "queries": "every real query of the sampled query blocks, for all five measures"},
         "roofline": {"kernel": "sparstar_block_mass", "bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
@@ -284,6 +306,136 @@ def uneven_lists(n_rows, n_k, r, k, seed=7, even=False, first=None):
     return row_ptr.astype(np.int32), np.concatenate(rows).astype(np.int32), counts
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or '' if unknown."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def time_calls(fns, reps, warmup, flush=None):
+    """Mean and median ms of each callable over `reps` rounds (HIP events on the current stream),
+    after `warmup` untimed rounds; `flush`, if given, runs untimed before every call."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for fn in fns:
+            if flush is not None:
+                flush()
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(reps)]
+    for r in range(reps):
+        for n, fn in enumerate(fns):
+            if flush is not None:
+                flush()
+            ev[r][n][0].record(stream)
+            fn()
+            ev[r][n][1].record(stream)
+    torch.cuda.synchronize()
+    out = []
+    for n in range(len(fns)):
+        t = np.array([ev[r][n][0].elapsed_time(ev[r][n][1]) for r in range(reps)])
+        out.append((float(t.mean()), float(np.median(t))))
+    return out
+
+
+def infinity_cache_flush(dev, mb=512):
+    """A callable that writes `mb` MiB of scratch, evicting the Infinity Cache (256 MB) and L2."""
+    import torch
+    buf = torch.empty((mb << 20) // 4, dtype=torch.float32, device=dev)
+    return lambda: buf.fill_(1.0)
+
+
+def scale_report(cfg, density, dev, reps=5, warmup=2, dense=False, inputs=None, flush=None):
+    """Per-kernel times of one scale at one density: pool_score (timed after an Infinity Cache flush),
+    select_blocks and bsa_fwd (or dense_attn_fwd), each with HIP events; executed TFLOP over real
+    tokens and the attention's fraction of the bf16 MFMA peak."""
+    import torch
+
+    from block_sparse_attention_aggregated_amd import inputs as I
+    from block_sparse_attention_aggregated_amd import sparstar as S
+    Q, K, V = inputs if inputs is not None else I.make_inputs(cfg, device=dev)
+    sc = S.Scale(cfg.len_text, cfg.len_ref, cfg.block, cfg.softmax_scale)
+    qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, density, cfg.policy)
+    out = torch.empty_like(Q)
+    ws = torch.empty((S.bsa_workspace_bytes(S.problem(Q, K, None, sc)) // 4,), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    rec = {"workload": cfg.name, "density": density, "policy": "first clip" if cfg.policy == 1 else "later clip",
+           "len_q": cfg.len_q, "len_k": cfg.len_k, "heads": cfg.heads, "block": cfg.block}
+    if dense:
+        (t_att, t_att_med), = time_calls([lambda: S.dense_attn_fwd(Q, K, V, sc, out=out, workspace=ws)], reps,
+                                         warmup)
+        flops = 4 * cfg.head_dim * cfg.batch * cfg.heads * cfg.len_q * cfg.len_k
+        rec.update(mode="dense", ms_attention=t_att, ms_attention_median=t_att_med, ms_scale=t_att)
+    else:
+        (t_pool, _), = time_calls([lambda: S.sparstar_pool_score(Q, K, sc, qp, kp, scores)], reps, warmup,
+                                  flush=flush)
+        (t_sel, _), (t_att, t_att_med) = time_calls(
+            [lambda: S.sparstar_select_blocks(scores, Q, K, sc, density, cfg.policy, row_ptr=rp, col_idx=ci),
+             lambda: S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, out=out, workspace=ws)], reps, warmup)
+        flops = exec_flops(cfg, rp, ci)
+        rec.update(mode="sparse", ms_pool_score=t_pool, ms_select=t_sel, ms_attention=t_att,
+                   ms_attention_median=t_att_med, ms_scale=t_pool + t_sel + t_att,
+                   scoring_gbs=scoring_bytes(cfg) / (t_pool * 1e-3) / 1e9,
+                   scoring_hbm_frac=scoring_bytes(cfg) / (t_pool * 1e-3) / 1e9 / PEAK_HBM_GBS)
+    rec["exec_tflop"] = flops / 1e12
+    rec["attention_tflops"] = flops / (t_att * 1e-3) / 1e12
+    rec["attention_bf16_peak_frac"] = rec["attention_tflops"] / PEAK_BF16_TFLOPS
+    rec["step_tflops"] = flops / (rec["ms_scale"] * 1e-3) / 1e12
+    return rec
+
+
+def north_star_report(dev, q720=None, log=lambda m: None):
+    """ms per scale, effective TFLOP/s and the fraction of the bf16 MFMA peak on every configuration:
+    192p (0.3), 480p (0.25), 720p at 0.1, 0.2, 0.4 and 1.0 (dense), the four-scale 720p sweep (0.2
+    each), and dense over sparse at 720p, density 0.1 (the analog of the pages' operator speed-up)."""
+    import torch
+
+    from block_sparse_attention_aggregated_amd import inputs as I
+    flush = infinity_cache_flush(dev)
+    rows = []
+    for cfg in (I.S192P, I.S480P):
+        log(f"report: {cfg.name}")
+        rows.append(scale_report(cfg, cfg.densities[0], dev, flush=flush))
+        torch.cuda.empty_cache()
+    inp = q720 if q720 is not None else I.make_inputs(I.S720P, device=dev)
+    for rho in (0.1, 0.2, 0.4):
+        log(f"report: 720p rho {rho}")
+        rows.append(scale_report(I.S720P, rho, dev, inputs=inp, flush=flush))
+    log("report: 720p dense")
+    rows.append(scale_report(I.S720P, 1.0, dev, reps=3, warmup=1, dense=True, inputs=inp))
+    del inp
+    torch.cuda.empty_cache()
+    sweep = []
+    for cfg in I.SWEEP:
+        log(f"report: {cfg.name}")
+        sweep.append(scale_report(cfg, 0.2, dev, flush=flush))
+        torch.cuda.empty_cache()
+    rows += sweep
+    r01 = next(r for r in rows if r["workload"] == "720p" and r["density"] == 0.1)
+    dense = next(r for r in rows if r.get("mode") == "dense")
+    flops = sum(r["exec_tflop"] for r in sweep)
+    ms = sum(r["ms_scale"] for r in sweep)
+    return {
+        "configs": rows,
+        "sweep_total": {"ms": ms, "exec_tflop": flops, "step_tflops": flops / (ms * 1e-3),
+                        "attention_bf16_peak_frac": flops / (sum(r["ms_attention"] for r in sweep) * 1e-3)
+                        / PEAK_BF16_TFLOPS},
+        "dense_over_sparse_720p_rho0.1": {"operator": dense["ms_attention"] / r01["ms_attention"],
+                                          "step": dense["ms_attention"] / r01["ms_scale"]},
+        "timing": "HIP events on the launch stream; 5 timed reps after 2 warm-up (dense: 3 after 1); "
+                  "pool_score timed after a 512 MiB scratch write that evicts the Infinity Cache",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -324,8 +476,9 @@ def main():
                   f"(uniform selection: {k})", file=sys.stderr, flush=True)
         out = torch.empty(Q.shape, dtype=od, device=dev)
         ws = torch.empty((S.balance_workspace_bytes(S.problem(Q, K, None, sc)) // 4,), dtype=torch.int32, device=dev)
+        qws = torch.empty((S.bsa_workspace_bytes(S.problem(Q, K, None, sc)) // 4,), dtype=torch.int32, device=dev)
         scales.append(dict(cfg=cfg, Q=Q, K=K, V=V, sc=sc, qp=qp, kp=kp, scores=scores, rp=rp, ci=ci, out=out,
-                           density=density, policy=cfg.policy, ws=ws))
+                           density=density, policy=cfg.policy, ws=ws, qws=qws))
     torch.cuda.synchronize()
     for s in scales:
         s["flops"] = (4 * s["cfg"].head_dim * s["cfg"].batch * s["cfg"].heads * s["cfg"].len_q * s["cfg"].len_k
@@ -340,7 +493,7 @@ def main():
                 if events is not None:
                     events[n][1].record(stream)
                     events[n][2].record(stream)
-                S.dense_attn_fwd(s["Q"], s["K"], s["V"], s["sc"], out=s["out"])
+                S.dense_attn_fwd(s["Q"], s["K"], s["V"], s["sc"], out=s["out"], workspace=s["qws"])
             else:
                 if args.fused_select:
                     S.sparstar_pool_blocks(s["Q"], s["K"], s["sc"], s["qp"], s["kp"])
@@ -360,7 +513,8 @@ def main():
                     S.sparstar_bsa_fwd_balanced(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"],
                                                 workspace=s["ws"])
                 else:
-                    S.sparstar_bsa_fwd(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"])
+                    S.sparstar_bsa_fwd(s["Q"], s["K"], s["V"], s["rp"], s["ci"], s["sc"], out=s["out"],
+                                       workspace=s["qws"])
             if events is not None:
                 events[n][3].record(stream)
 
@@ -439,6 +593,11 @@ def main():
                         and not args.dense and not args.uneven else None),
         },
     }
+    if rec["roofline"]["traffic"] is not None:
+        rec["roofline"]["traffic_source"] = (
+            f"not measured in this run: {os.path.relpath(TRAFFIC_FILE, ROOT)}, rocprofv3 FETCH_SIZE and WRITE_SIZE "
+            f"of one launch scaled by a plain device copy, taken on this kernel source (sha256 "
+            f"{traffic['kernel_sha256'][:16]}...)")
     if not args.dense and not args.fused_select and len(scales) == 1:
         p = per_scale[0]
         rec["scoring_roofline"] = {"kernel": "sparstar_pool_score", "bound": "hbm",
@@ -453,6 +612,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         rec["calib_copy_bytes"] = 2 * n * 4
+    plain = not (args.dense or args.uneven or args.balanced or args.fused_select or args.out_dtype or
+                 args.density is not None)
+    if args.workload == "720p" and plain and not args.no_report:
+        def log(m):
+            print(f"# {m}", file=sys.stderr, flush=True)
+        s = scales[0]
+        rec["north_star_report"] = north_star_report(dev, q720=(s["Q"], s["K"], s["V"]), log=log)
     if not args.no_cpu_baseline and not args.dense and not args.uneven:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         s = scales[-1]

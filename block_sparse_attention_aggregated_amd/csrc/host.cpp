@@ -185,17 +185,69 @@ sparstar_status attn_common(const sparstar_problem* p, const void* q, const void
   return SPARSTAR_OK;
 }
 
-sparstar_status run_attn(const sparstar::AttnArgs& a, hipStream_t st) {
+// Which attention kernel a problem runs on: the bf16 MFMA kernel takes bf16 inputs
+// with D = 128 whose in-head byte offsets fit 32 bits; everything else runs the
+// float32 kernel.
+bool uses_mfma(const sparstar_problem* p) {
+  const int64_t L_k = p->len_text + p->len_ref + p->len_q;
+  const bool small_extent =
+      (L_k + 256) * std::max(p->k_stride[2], p->v_stride[2]) * 2 < ((int64_t)1 << 31) &&
+      (p->len_q + 256) * std::max(p->q_stride[2], p->o_stride[2]) * 4 < ((int64_t)1 << 31);
+  return p->dtype == SPARSTAR_BF16 && p->head_dim == 128 && small_extent;
+}
+
+sparstar_status run_attn(const sparstar_problem* p, const sparstar::AttnArgs& a, int* counters,
+                         hipStream_t st) {
   const int64_t rows = (int64_t)a.g.B * a.g.H * a.g.n_q;
   if (rows == 0) return ok();
   sparstar_status s = check_device();
   if (s != SPARSTAR_OK) return s;
-  // The MFMA kernel keeps in-head byte offsets in 32 bits.
-  const bool small_extent = (a.g.L_k + 256) * std::max(a.ks_t, a.vs_t) * 2 < ((int64_t)1 << 31) &&
-                            (a.g.L_q + 256) * std::max(a.qs_t, a.os_t) * 4 < ((int64_t)1 << 31);
-  const bool mfma = a.dtype == SPARSTAR_BF16 && a.g.D == 128 && small_extent;
-  return launched(mfma ? sparstar::launch_attn_mfma(a, st) : sparstar::launch_attn_simt(a, st),
+  const bool mfma = uses_mfma(p);
+  return launched(mfma ? sparstar::launch_attn_mfma(a, counters, st) : sparstar::launch_attn_simt(a, st),
                   mfma ? "attention (bf16 MFMA) launch" : "attention (float32) launch");
+}
+
+
+// Workspace of the balanced call: the dynamic queues' counters, then the row order.
+constexpr int64_t kCounterBytes = 256;
+static_assert(sparstar::kAttnCounters * 4 <= kCounterBytes, "counter block too small");
+
+int64_t balance_workspace_bytes(const sparstar_problem* p) {
+  return kCounterBytes + sparstar::row_order_entries((int64_t)p->batch * p->heads,
+                                                     (int32_t)ceil_div(p->len_q, p->block), p->block) *
+                             (int64_t)sizeof(int32_t);
+}
+
+sparstar_status bsa_fwd_balanced_impl(const sparstar_problem* p, const void* q, const void* k, const void* v,
+                                      const int32_t* row_ptr, const int32_t* col_idx, int64_t col_idx_len, void* out,
+                                      float* lse, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  sparstar::AttnArgs a;
+  sparstar_status s = attn_common(p, q, k, v, out, a);
+  if (s != SPARSTAR_OK) return s;
+  if (!row_ptr || !col_idx) return fail(SPARSTAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
+  if (col_idx_len < 0) return fail(SPARSTAR_ERR_SHAPE, "col_idx_len must be >= 0");
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+    return fail(SPARSTAR_ERR_LAYOUT, "row_ptr, col_idx, lse and workspace must be 4-byte aligned");
+  const int64_t rows = (int64_t)a.g.B * a.g.H * a.g.n_q;
+  const int64_t need = balance_workspace_bytes(p);
+  if (workspace_bytes < need)
+    return fail(SPARSTAR_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  a.lse = lse;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_idx_len = col_idx_len;
+  if (rows == 0) return ok();
+  if ((s = check_device()) != SPARSTAR_OK) return s;
+  int* counters = static_cast<int*>(workspace);
+  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kCounterBytes);
+  s = launched(sparstar::launch_row_order(row_ptr, (int64_t)a.g.B * a.g.H, a.g.n_q, a.g.b, col_idx_len, order,
+                                          stream),
+               "row order launch");
+  if (s != SPARSTAR_OK) return s;
+  a.row_order = order;
+  return run_attn(p, a, counters, stream);
 }
 
 }  // namespace
@@ -239,6 +291,11 @@ int64_t sparstar_select_nnz(const sparstar_problem* p, double density, int32_t p
   const int64_t per_row = sparstar_blocks_per_row(p, density, policy);
   if (per_row < 0) return -1;
   return (int64_t)p->batch * p->heads * ceil_div(p->len_q, p->block) * per_row;
+}
+
+int32_t sparstar_attention_kernel(const sparstar_problem* p) {
+  if (check_problem_impl(p) != SPARSTAR_OK) return -1;
+  return uses_mfma(p) ? SPARSTAR_KERNEL_MFMA_BF16 : SPARSTAR_KERNEL_F32;
 }
 
 const char* sparstar_status_string(sparstar_status s) {
@@ -392,9 +449,14 @@ sparstar_status sparstar_score_select(const sparstar_problem* p, const float* q_
   });
 }
 
+int64_t sparstar_bsa_workspace_bytes(const sparstar_problem* p) {
+  if (check_problem_impl(p) != SPARSTAR_OK) return -1;
+  return kCounterBytes;
+}
+
 sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const void* k, const void* v,
                                  const int32_t* row_ptr, const int32_t* col_idx, int64_t col_idx_len,
-                                 void* out, float* lse, void* stream) {
+                                 void* out, float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
   return guarded([&]() -> sparstar_status {
     sparstar::AttnArgs a;
     sparstar_status s = attn_common(p, q, k, v, out, a);
@@ -402,28 +464,35 @@ sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const
     if (!row_ptr || !col_idx) return fail(SPARSTAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
     if (col_idx_len < 0) return fail(SPARSTAR_ERR_SHAPE, "col_idx_len must be >= 0");
     if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
-        (reinterpret_cast<uintptr_t>(lse) & 3u))
-      return fail(SPARSTAR_ERR_LAYOUT, "row_ptr, col_idx and lse must be 4-byte aligned");
+        (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+      return fail(SPARSTAR_ERR_LAYOUT, "row_ptr, col_idx, lse and workspace must be 4-byte aligned");
+    if (workspace && workspace_bytes < kCounterBytes)
+      return fail(SPARSTAR_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                  (long long)kCounterBytes);
     a.lse = lse;
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
     a.col_idx_len = col_idx_len;
-    return run_attn(a, (hipStream_t)stream);
+    return run_attn(p, a, static_cast<int*>(workspace), (hipStream_t)stream);
   });
 }
 
 sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const void* k, const void* v,
-                               void* out, float* lse, void* stream) {
+                               void* out, float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
   return guarded([&]() -> sparstar_status {
     sparstar::AttnArgs a;
     sparstar_status s = attn_common(p, q, k, v, out, a);
     if (s != SPARSTAR_OK) return s;
-    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(SPARSTAR_ERR_LAYOUT, "lse must be 4-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+      return fail(SPARSTAR_ERR_LAYOUT, "lse and workspace must be 4-byte aligned");
+    if (workspace && workspace_bytes < kCounterBytes)
+      return fail(SPARSTAR_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                  (long long)kCounterBytes);
     a.lse = lse;
     a.row_ptr = nullptr;
     a.col_idx = nullptr;
     a.col_idx_len = 0;
-    return run_attn(a, (hipStream_t)stream);
+    return run_attn(p, a, static_cast<int*>(workspace), (hipStream_t)stream);
   });
 }
 
@@ -534,9 +603,7 @@ sparstar_status sparstar_token_topk_mass(const sparstar_problem* p, const void* 
 
 int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p) {
   if (check_problem_impl(p) != SPARSTAR_OK) return -1;
-  return sparstar::row_order_entries((int64_t)p->batch * p->heads, (int32_t)ceil_div(p->len_q, p->block),
-                                     p->block) *
-         (int64_t)sizeof(int32_t);
+  return balance_workspace_bytes(p);
 }
 
 sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void* q, const void* k, const void* v,
@@ -544,34 +611,9 @@ sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void*
                                           void* out, float* lse, void* workspace, int64_t workspace_bytes,
                                           void* stream) {
   return guarded([&]() -> sparstar_status {
-    sparstar::AttnArgs a;
-    sparstar_status s = attn_common(p, q, k, v, out, a);
-    if (s != SPARSTAR_OK) return s;
-    if (!row_ptr || !col_idx || !workspace)
-      return fail(SPARSTAR_ERR_NULL, "row_ptr, col_idx and workspace must be non-NULL");
-    if (col_idx_len < 0) return fail(SPARSTAR_ERR_SHAPE, "col_idx_len must be >= 0");
-    if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
-        (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
-      return fail(SPARSTAR_ERR_LAYOUT, "row_ptr, col_idx, lse and workspace must be 4-byte aligned");
-    const int64_t rows = (int64_t)a.g.B * a.g.H * a.g.n_q;
-    const int64_t need =
-        sparstar::row_order_entries((int64_t)a.g.B * a.g.H, a.g.n_q, a.g.b) * (int64_t)sizeof(int32_t);
-    if (workspace_bytes < need)
-      return fail(SPARSTAR_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
-                  (long long)need);
-    a.lse = lse;
-    a.row_ptr = row_ptr;
-    a.col_idx = col_idx;
-    a.col_idx_len = col_idx_len;
-    if (rows == 0) return ok();
-    if ((s = check_device()) != SPARSTAR_OK) return s;
-    int32_t* order = static_cast<int32_t*>(workspace);
-    s = launched(sparstar::launch_row_order(row_ptr, (int64_t)a.g.B * a.g.H, a.g.n_q, a.g.b, col_idx_len, order,
-                                            (hipStream_t)stream),
-                 "row order launch");
-    if (s != SPARSTAR_OK) return s;
-    a.row_order = order;
-    return run_attn(a, (hipStream_t)stream);
+    if (!workspace) return fail(SPARSTAR_ERR_NULL, "workspace must be non-NULL");
+    return bsa_fwd_balanced_impl(p, q, k, v, row_ptr, col_idx, col_idx_len, out, lse, workspace, workspace_bytes,
+                                 (hipStream_t)stream);
   });
 }
 

@@ -136,7 +136,11 @@ int64_t row_order_entries(int64_t bh, int32_t n_q, int32_t b);
 hipError_t launch_row_order(const int32_t* row_ptr, int64_t bh, int32_t n_q, int32_t b, int64_t col_idx_len,
                             int32_t* order, hipStream_t s);
 // bf16 inputs, D = 128, b = 64, 128 or 256, in-head K/V byte offsets below 2^31 (MFMA path).
-hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+// A persistent grid: with counters (kAttnCounters ints, zeroed by the launch itself) the
+// row queues are dynamic (atomic pops, idle workgroups take other XCDs' rows); without,
+// each workgroup runs a fixed share of its XCD's queue.
+constexpr int kAttnCounters = kXcds;
+hipError_t launch_attn_mfma(const AttnArgs& a, int* counters, hipStream_t s);
 // Any supported shape/dtype (float32 path).
 hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t s);
 

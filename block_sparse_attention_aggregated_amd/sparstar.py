@@ -20,6 +20,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparstar.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_LAYOUT, ERR_DENSITY, ERR_CAPACITY, ERR_HIP = range(8)
+KERNEL_MFMA_BF16, KERNEL_F32 = 0, 1
 BF16, F32 = 0, 1
 POLICY_LATER_CLIP, POLICY_FIRST_CLIP = 0, 1
 
@@ -63,10 +64,13 @@ _SIGS = {
     "sparstar_pool_blocks": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "sparstar_score_select": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_dbl, _c_i32, _c_vp, _c_vp,
                                        _c_i64, _c_vp]),
+    "sparstar_bsa_workspace_bytes": (_c_i64, [ctypes.POINTER(Problem)]),
     "sparstar_bsa_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
-                                  _c_vp, _c_vp, _c_vp]),
-    "dense_attn_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+                                  _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "dense_attn_fwd": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
+                                _c_vp]),
     "sparstar_balance_workspace_bytes": (_c_i64, [ctypes.POINTER(Problem)]),
+    "sparstar_attention_kernel": (_c_i32, [ctypes.POINTER(Problem)]),
     "sparstar_bsa_fwd_balanced": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
                                            _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "sparstar_block_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
@@ -190,6 +194,11 @@ def balance_workspace_bytes(p: Problem) -> int:
     return lib().sparstar_balance_workspace_bytes(ctypes.byref(p))
 
 
+def attention_kernel(p: Problem) -> int:
+    """KERNEL_MFMA_BF16 or KERNEL_F32: which attention kernel the problem runs on (-1 if invalid)."""
+    return lib().sparstar_attention_kernel(ctypes.byref(p))
+
+
 def status_string(s: int) -> str:
     return lib().sparstar_status_string(s).decode()
 
@@ -285,10 +294,17 @@ def sparstar_score_select(q_pool: torch.Tensor, k_pool: torch.Tensor, q: torch.T
     return row_ptr, col_idx[:nnz]
 
 
+def bsa_workspace_bytes(p: Problem) -> int:
+    return lib().sparstar_bsa_workspace_bytes(ctypes.byref(p))
+
+
 def sparstar_bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
                      col_idx: torch.Tensor, scale: Scale, out=None, out_dtype=None,
-                     return_lse: bool = False):
-    """Block-sparse attention forward over the CSR block lists."""
+                     return_lse: bool = False, workspace="auto"):
+    """Block-sparse attention forward over the CSR block lists.
+
+    workspace: "auto" allocates the row-queue counters with torch (persistent grid, dynamic
+    queues), a device tensor is used as given, None runs one workgroup per row (no workspace)."""
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     p = problem(q, k, v, scale, out=out)
@@ -298,8 +314,12 @@ def sparstar_bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr:
     rows = q.shape[0] * q.shape[1] * num_q_blocks(p)
     if row_ptr.numel() != rows + 1 or not row_ptr.is_contiguous() or not col_idx.is_contiguous():
         raise SparstarError(ERR_SHAPE, f"row_ptr must hold {rows + 1} entries, contiguous")
+    if isinstance(workspace, str):
+        workspace = torch.empty((max(bsa_workspace_bytes(p), 4) // 4,), dtype=torch.int32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sparstar_bsa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
-                                  col_idx.numel(), _ptr(out), _ptr(lse), _stream(q.device)))
+                                  col_idx.numel(), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                  _stream(q.device)))
     return (out, lse) if return_lse else out
 
 
@@ -326,14 +346,18 @@ def sparstar_bsa_fwd_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def dense_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Scale, out=None,
-                   out_dtype=None, return_lse: bool = False):
-    """Dense attention forward over every key block (the density-1 baseline)."""
+                   out_dtype=None, return_lse: bool = False, workspace="auto"):
+    """Dense attention forward over every key block (the density-1 baseline); workspace as for
+    sparstar_bsa_fwd."""
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     p = problem(q, k, v, scale, out=out)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    if isinstance(workspace, str):
+        workspace = torch.empty((max(bsa_workspace_bytes(p), 4) // 4,), dtype=torch.int32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dense_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                _stream(q.device)))
+                                _ptr(workspace), ws_bytes, _stream(q.device)))
     return (out, lse) if return_lse else out
 
 

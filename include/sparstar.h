@@ -168,6 +168,10 @@ sparstar_status sparstar_select_blocks(const sparstar_problem* p, const float* s
                                        double density, int32_t policy, int32_t* row_ptr,
                                        int32_t* col_idx, int64_t col_idx_capacity, void* stream);
 
+/* Bytes of device workspace sparstar_bsa_fwd and dense_attn_fwd take for their row
+ * queues (256: the counters of the per-XCD queues); -1 if the problem is invalid. */
+int64_t sparstar_bsa_workspace_bytes(const sparstar_problem* p);
+
 /* Step 4 (section 5 "Forward-Only Sparse Execution", "Complexity and Scope").
  * Each query t of block i gets o_t = sum_s softmax_s(sigma * q_t.k_s) v_s over the
  * real key tokens s (< L_k) of the blocks col_idx[row_ptr[r] .. row_ptr[r+1]),
@@ -178,39 +182,64 @@ sparstar_status sparstar_select_blocks(const sparstar_problem* p, const float* s
  *   row_ptr  : in, int32 [B*H*n_q + 1];  col_idx: in, int32 [col_idx_len].
  *   out      : out, p->out_dtype with p->o_stride; rows >= L_q are not written.
  *   lse      : out, nullable, float32 [B, H, L_q] contiguous: sigma*max + log(sum exp).
+ *   workspace: nullable device buffer of at least sparstar_bsa_workspace_bytes bytes,
+ *              owned by the caller (SPARSTAR_ERR_CAPACITY if smaller).  With it, a
+ *              persistent grid of as many workgroups as fit on the GPU at once takes
+ *              the rows from per-XCD queues with atomic counters, which the call
+ *              clears itself (a kernel, no memset), and a workgroup whose XCD has no
+ *              rows left takes rows from the other XCDs' queues; two calls must not
+ *              share a workspace while either runs.  With NULL (and any
+ *              workspace_bytes), one workgroup per row, handed to the XCDs by the
+ *              hardware dispatcher.  The outputs are the same, bit for bit, either way.
  * bf16 inputs with D = 128 run on bf16 MFMA with float32 softmax and accumulation
  * for every block size (64, 128, 256: the block sizes of appendix D.2 "Block-Size
- * Ablation"); D = 64 and float32 inputs run a float32 kernel. */
+ * Ablation").
+ * D = 64 and float32 inputs run a float32 kernel (sparstar_attention_kernel tells
+ * which), which ignores the workspace. */
 sparstar_status sparstar_bsa_fwd(const sparstar_problem* p, const void* q, const void* k,
                                  const void* v, const int32_t* row_ptr, const int32_t* col_idx,
-                                 int64_t col_idx_len, void* out, float* lse, void* stream);
+                                 int64_t col_idx_len, void* out, float* lse, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+/* Which kernel sparstar_bsa_fwd, sparstar_bsa_fwd_balanced and dense_attn_fwd run for a
+ * problem: SPARSTAR_KERNEL_MFMA_BF16 for bf16 inputs with head_dim 128 whose in-head
+ * byte offsets (L + 256 tokens at the largest token stride) stay below 2^31;
+ * SPARSTAR_KERNEL_F32 (a float32 kernel, one thread per query: correct, not tuned)
+ * for every other valid problem, bf16 inputs with head_dim 64 included; -1 if the
+ * problem is invalid.  Host only. */
+typedef enum { SPARSTAR_KERNEL_MFMA_BF16 = 0, SPARSTAR_KERNEL_F32 = 1 } sparstar_kernel;
+int32_t sparstar_attention_kernel(const sparstar_problem* p);
 
 /* Dense attention forward (every key block of every row): the density-1 baseline
  * that the sparse operator is compared with (section 6 "End-to-end efficiency").
- * Arguments as for sparstar_bsa_fwd without the block lists. */
+ * Arguments, workspace included, as for sparstar_bsa_fwd without the block lists. */
 sparstar_status dense_attn_fwd(const sparstar_problem* p, const void* q, const void* k,
-                               const void* v, void* out, float* lse, void* stream);
+                               const void* v, void* out, float* lse, void* workspace,
+                               int64_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace sparstar_bsa_fwd_balanced needs: 4 * B*H*S*ceil(n_q/S),
- * with S = 4 segments per head at blocks 128 and 256 when B*H is even, and S = 8
- * otherwise; -1 if the problem is invalid. */
+/* Bytes of device workspace sparstar_bsa_fwd_balanced needs: 256 bytes of row-queue
+ * counters followed by the row order, 4 * B*H*S*ceil(n_q/S) bytes, with S = 4 segments
+ * per head at blocks 128 and 256 when B*H is even, and S = 8 otherwise; -1 if the
+ * problem is invalid. */
 int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p);
 
 /* sparstar_bsa_fwd for block lists of uneven length (section 5 "Forward-Only Sparse
  * Execution": the lists are per query block and their lengths are the caller's).
  * The attention runs the query blocks of a head in S contiguous segments of
  * ceil(n_q/S) blocks, one per XCD (S = 4 at blocks 128 and 256 with an even B*H: two
- * heads at a time; S = 8 otherwise: one head at a time), heads in order; here the rows of each
- * segment are first ordered by list length, longest first and stably (equal lengths
- * keep their order), into `workspace` (a device buffer of at least
- * sparstar_balance_workspace_bytes, owned by the caller; on return it holds the
- * order: entry (b*H + h)*S*ceil(n_q/S) + x*ceil(n_q/S) + m is the query block of the
- * m-th row of segment x, -1 past the segment's end), so that no long row is started
- * last.  Every row is computed exactly as by sparstar_bsa_fwd: the outputs
- * are the same, bit for bit.  The order is used by the bf16 MFMA kernel; the float32
- * kernel (float32 inputs, D = 64, or K/V extents of 2^31 bytes or more per head) runs
- * the rows in their natural order, and the workspace is still written.
- * SPARSTAR_ERR_CAPACITY if the workspace is too small.
+ * heads at a time; S = 8 otherwise: one head at a time), heads in order.  Here the rows of
+ * each segment are first ordered by list length, longest first and stably (equal lengths
+ * keep their order), and the persistent workgroups take rows from per-XCD queues with
+ * atomic counters: a workgroup whose XCD's queue is empty takes rows from the other
+ * XCDs' queues, so no XCD idles while another still has rows.  `workspace` is a device
+ * buffer of at least sparstar_balance_workspace_bytes, owned by the caller; the call
+ * clears the counters itself (a kernel, no memset).  On return bytes [0, 256) hold the
+ * counters and from byte 256 on the order: entry (b*H + h)*S*ceil(n_q/S) + x*ceil(n_q/S) + m
+ * is the query block of the m-th row of segment x, -1 past the segment's end.  Every row
+ * is computed exactly as by sparstar_bsa_fwd: the outputs are the same, bit for bit.  The
+ * queues and the order are used by the bf16 MFMA kernel; the float32 kernel (see
+ * sparstar_attention_kernel) runs the rows in their natural order, and the workspace is
+ * still written.  SPARSTAR_ERR_CAPACITY if the workspace is too small.
  * Two calls must not share a workspace while either runs. */
 sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void* q, const void* k,
                                           const void* v, const int32_t* row_ptr, const int32_t* col_idx,

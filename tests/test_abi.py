@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 21
+    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 23
     assert {"sparstar_pool_blocks", "sparstar_score_select"} <= set(names)
     assert {"sparstar_block_mass", "sparstar_selection_mass", "sparstar_window_scores",
             "sparstar_token_topk_mass"} <= set(names)
@@ -130,9 +130,9 @@ def test_problem_validation(mutate, code):
     assert st == code and msg
     st, msg = _status(L.sparstar_select_blocks, ctypes.byref(p), b, 0.3, 0, b, b, 10**9, None)
     assert st == code and msg
-    st, msg = _status(L.sparstar_bsa_fwd, ctypes.byref(p), b, b, b, b, b, 10, b, None, None)
+    st, msg = _status(L.sparstar_bsa_fwd, ctypes.byref(p), b, b, b, b, b, 10, b, None, b, 256, None)
     assert st == code and msg
-    st, msg = _status(L.dense_attn_fwd, ctypes.byref(p), b, b, b, b, None, None)
+    st, msg = _status(L.dense_attn_fwd, ctypes.byref(p), b, b, b, b, None, b, 256, None)
     assert st == code and msg
 
 
@@ -145,12 +145,18 @@ def test_null_and_alignment_and_density_and_capacity():
     assert L.sparstar_pool_score(None, b, b, b, b, b, None) == S.ERR_NULL
     assert L.sparstar_pool_score(ctypes.byref(p), None, b, b, b, b, None) == S.ERR_NULL
     assert L.sparstar_pool_score(ctypes.byref(p), b, b, b, b, odd, None) == S.ERR_LAYOUT
-    assert L.dense_attn_fwd(ctypes.byref(p), b, b, None, b, None, None) == S.ERR_NULL
-    assert L.dense_attn_fwd(ctypes.byref(p), b, odd, b, b, None, None) == S.ERR_LAYOUT
-    assert L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, None, b, 10, b, None, None) == S.ERR_NULL
-    assert L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, b, b, -1, b, None, None) == S.ERR_SHAPE
-    assert L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, b, b, 10, b, ctypes.c_void_p(BOGUS + 1), None) \
+    assert L.dense_attn_fwd(ctypes.byref(p), b, b, None, b, None, b, 256, None) == S.ERR_NULL
+    assert L.dense_attn_fwd(ctypes.byref(p), b, odd, b, b, None, b, 256, None) == S.ERR_LAYOUT
+    assert L.dense_attn_fwd(ctypes.byref(p), b, b, b, b, None, odd, 256, None) == S.ERR_LAYOUT
+    assert L.dense_attn_fwd(ctypes.byref(p), b, b, b, b, None, b, 8, None) == S.ERR_CAPACITY
+    assert L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, None, b, 10, b, None, b, 256, None) == S.ERR_NULL
+    assert L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, b, b, -1, b, None, b, 256, None) == S.ERR_SHAPE
+    assert L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, b, b, 10, b, ctypes.c_void_p(BOGUS + 1), b, 256, None) \
         == S.ERR_LAYOUT
+    assert L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, b, b, 10, b, None, odd, 256, None) == S.ERR_LAYOUT
+    assert S.bsa_workspace_bytes(p) == 256
+    st = L.sparstar_bsa_fwd(ctypes.byref(p), b, b, b, b, b, 10, b, None, b, 255, None)
+    assert st == S.ERR_CAPACITY and "workspace" in S.last_error()
     for rho in (0.0, -1.0, 1.5, float("nan")):
         assert L.sparstar_select_blocks(ctypes.byref(p), b, rho, 0, b, b, 10**9, None) == S.ERR_DENSITY
     assert L.sparstar_select_blocks(ctypes.byref(p), b, 0.3, 5, b, b, 10**9, None) == S.ERR_UNSUPPORTED
@@ -203,18 +209,19 @@ def test_mass_entry_points_validate_before_any_device_call():
     assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, None, 4, 0, 0, b, None) == S.ERR_NULL
     assert L.sparstar_token_topk_mass(ctypes.byref(p), b, b, b, ctypes.c_void_p(BOGUS + 4), 4, 0, 0, b,
                                       None) == S.ERR_LAYOUT
-    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p)) == 16 * 40 * 4     # 4 segments of 10 blocks
+    # 256 bytes of queue counters, then the row order
+    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p)) == 256 + 16 * 40 * 4   # 4 segments of 10 blocks
     p64 = _prob(I.S192P_B64)                                                     # n_q = 79: 8 segments of 10
-    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p64)) == 16 * 8 * 10 * 4
+    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p64)) == 256 + 16 * 8 * 10 * 4
     p256 = _prob(I.S192P_B256)                                                   # n_q = 20: 4 segments of 5
-    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p256)) == 16 * 4 * 5 * 4
+    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p256)) == 256 + 16 * 4 * 5 * 4
     p.heads = 15                                                                 # odd head count: 8 segments of 5
-    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p)) == 15 * 8 * 5 * 4
+    assert L.sparstar_balance_workspace_bytes(ctypes.byref(p)) == 256 + 15 * 8 * 5 * 4
     p.heads = 16
     assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, 10, b, None, None, 1 << 20, None) \
         == S.ERR_NULL
-    assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, 10, b, None, b, 16 * 40 * 4 - 1, None) \
-        == S.ERR_CAPACITY
+    assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, 10, b, None, b, 256 + 16 * 40 * 4 - 1,
+                                       None) == S.ERR_CAPACITY
     assert L.sparstar_bsa_fwd_balanced(ctypes.byref(p), b, b, b, b, b, -1, b, None, b, 1 << 20, None) \
         == S.ERR_SHAPE
     # nothing listed: nothing to do, no device needed
@@ -228,6 +235,22 @@ def test_too_many_candidates_is_refused():
     b = ctypes.c_void_p(BOGUS)
     st = S.lib().sparstar_select_blocks(ctypes.byref(p), b, 0.2, 0, b, b, 10**12, None)
     assert st == S.ERR_UNSUPPORTED
+
+
+def test_attention_kernel_choice():
+    """The host names the kernel a problem runs on: bf16 at head_dim 128 on the MFMA kernel,
+    float32 inputs and head_dim 64 (bf16 too) on the float32 kernel; invalid problems -1."""
+    assert S.attention_kernel(_prob(I.S720P)) == S.KERNEL_MFMA_BF16
+    assert S.attention_kernel(_prob(I.S720P_B64)) == S.KERNEL_MFMA_BF16
+    assert S.attention_kernel(_prob(I.TINY, S.F32)) == S.KERNEL_F32
+    assert S.attention_kernel(_prob(I.TINY, S.BF16)) == S.KERNEL_F32          # head_dim 64
+    assert S.attention_kernel(_prob(I.S192P, S.F32)) == S.KERNEL_F32
+    wide = _prob(I.S192P)
+    wide.k_stride[2] = 1 << 18                                               # K/V extents past 2^31 bytes
+    assert S.attention_kernel(wide) == S.KERNEL_F32
+    bad = _prob(I.S192P)
+    bad.block = 96
+    assert S.attention_kernel(bad) == -1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

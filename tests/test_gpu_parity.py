@@ -161,6 +161,7 @@ def _check_attention(cfg, Q, K, V, rows_lists, out, lse, heads, sample_rows, bf1
     (I.S192P, 0.3, torch.bfloat16, None, None),
     (I.S192P, 0.3, torch.float32, [0, 7, 15], None),
     (I.S480P, 0.25, torch.bfloat16, [0, 9, 23], 12),
+    (I.S480P, 0.25, torch.float32, [0, 9, 23], 12),
 ])
 def test_bsa_parity_on_gpu_csr(cfg, rho, out_dtype, heads, nsample):
     """bsa_fwd against oracle attention over the GPU's own block lists."""
@@ -362,12 +363,12 @@ def test_balanced_equals_plain_bitwise(D, b, dtype, H):
     a, la = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True)
     nseg = 4 if b != 64 and H % 2 == 0 else 8               # segments per head
     per = -(-nq // nseg)
-    ws = torch.full((H * nseg * per,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.full((64 + H * nseg * per,), -7, dtype=torch.int32, device=DEV)   # counters, then the order
     assert S.balance_workspace_bytes(S.problem(Q, K, V, scale)) == ws.numel() * 4
     c, lc = S.sparstar_bsa_fwd_balanced(Q, K, V, rp_t, ci_t, scale, return_lse=True, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, c) and torch.equal(la, lc)
-    order = ws.cpu().numpy().reshape(H, nseg, per)
+    order = ws[64:].cpu().numpy().reshape(H, nseg, per)
     lens = np.diff(rp).reshape(H, nq)
     for h in range(H):
         for x in range(nseg):
@@ -380,6 +381,40 @@ def test_balanced_equals_plain_bitwise(D, b, dtype, H):
             for u in range(len(got) - 1):                       # stable among equal lengths
                 if ln[u] == ln[u + 1]:
                     assert got[u] < got[u + 1]
+
+
+@pytest.mark.parametrize("b", [64, 128, 256])
+def test_static_and_dynamic_queues_bitwise(b):
+    """The two ways of handing out rows (one workgroup per row without a workspace, a persistent grid
+    on per-XCD atomic queues with one) compute every row the same way: equal bit for bit, on the
+    selection's lists, on irregular ones (empty rows, duplicates, out-of-range entries) and dense."""
+    L_text, L_ref, L_q, H = 64, 700, 900, 3
+    print_case("static vs dynamic queues", b)
+    Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, 128, torch.bfloat16, seed=21)
+    scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(128))
+    (a, la), (_, rp, ci) = S.scale_forward(Q, K, V, scale, 0.3, return_lse=True)
+    c, lc = S.sparstar_bsa_fwd(Q, K, V, rp, ci, scale, return_lse=True, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c) and torch.equal(la, lc)
+    nq, nk = O.num_blocks(L_q, b), O.num_blocks(L_text + L_ref + L_q, b)
+    rng = np.random.default_rng(4)
+    lists = [np.zeros(0, np.int64) if r % 5 == 0 else np.array([1, 1, -3, nk]) if r % 5 == 1
+             else np.sort(rng.choice(nk, rng.integers(1, nk + 1), replace=False)) for r in range(H * nq)]
+    rp_np = np.zeros(len(lists) + 1, dtype=np.int32)
+    rp_np[1:] = np.cumsum([len(x) for x in lists])
+    rp_t = torch.from_numpy(rp_np).to(DEV)
+    ci_t = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(DEV)
+    ws = torch.full((64,), 12345, dtype=torch.int32, device=DEV)        # stale counters: the call clears them
+    d, ld = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True, workspace=ws)
+    e, le = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(d, e) and torch.equal(ld, le)
+    # the dense path: persistent queues and one workgroup per row
+    ws.fill_(-5)
+    f, lf = S.dense_attn_fwd(Q, K, V, scale, return_lse=True, workspace=ws)
+    g, lg = S.dense_attn_fwd(Q, K, V, scale, return_lse=True, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(f, g) and torch.equal(lf, lg)
 
 
 def test_balanced_on_the_selection():
@@ -485,6 +520,10 @@ def test_clip_schedule_end_to_end(name, heads):
         rng = np.random.default_rng(200 + h)
         return sorted({0, nq - 1, *rng.choice(nq, 4, replace=False).tolist()})
     _check_attention(cfg, Q, K, V, lists, out, lse, list(check_heads), sampler, True)
+    # the same kernel on the same lists with a float32-stored output: the plain gate
+    out32 = S.sparstar_bsa_fwd(Q, K, V, rp, ci, scale_of(cfg), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_attention(cfg, Q, K, V, lists, out32, None, list(check_heads), sampler, True)
 
 
 # ---------------------------------------------------------------- block sizes 64 and 256
@@ -609,6 +648,37 @@ def test_fused_score_select_equals_unfused_bitwise(name, rho):
     _fused_equals_unfused(Q, K, scale_of(cfg), rho, cfg.policy)
 
 
+@pytest.mark.parametrize("name,heads", [("192p", None), ("480p", [0, 12, 23]), ("720p", [0, 15, 31]),
+                                        ("720p_clip1_s1", [0, 31])])
+def test_fused_score_select_against_oracle(name, heads):
+    """The fused kernel's block lists against the oracle directly: pooled blocks within the pooling
+    bound, and every row of the checked heads equal to the oracle's selection on its float64 scores
+    but for near-ties (within 1e-4 relative of the row's k-th best score)."""
+    cfg = I.WORKLOADS[name]
+    rho = cfg.densities[0] if name != "720p" else 0.2
+    print_case("fused select vs oracle", cfg.name, rho, cfg.policy)
+    Q, K, V = inputs(cfg)
+    sc = scale_of(cfg)
+    qp, kp = S.sparstar_pool_blocks(Q, K, sc)
+    rp, ci = S.sparstar_score_select(qp, kp, Q, K, sc, rho, cfg.policy)
+    torch.cuda.synchronize()
+    lists = csr_rows(rp, ci)
+    b = cfg.block
+    nq = O.num_blocks(cfg.len_q, b)
+    R, C = O.retained_and_candidates(cfg.len_text, cfg.len_ref, cfg.len_q, b, cfg.policy)
+    kk = O.budget(len(C), rho)
+    swaps = 0
+    for h in (range(cfg.heads) if heads is None else heads):
+        qbar, kbar = O.pool_blocks(head_np(Q, h), b), O.pool_blocks(head_np(K, h), b)
+        assert np.max(np.abs(to_f64(qp[0, h]) - qbar)) < 2e-6 * max(1.0, np.abs(qbar).max())
+        assert np.max(np.abs(to_f64(kp[0, h]) - kbar)) < 2e-6 * max(1.0, np.abs(kbar).max())
+        S_ref = O.block_scores(qbar, kbar, cfg.softmax_scale)
+        ref_sets = O.select_blocks(S_ref, R, C, kk)
+        for i in range(nq):
+            swaps += compare_row_selection(lists[h * nq + i], ref_sets[i], S_ref[i], len(R), kk)
+    print(f"fused selection: near-tie swaps {swaps}")
+
+
 def test_fused_score_select_random_shapes():
     """The seeded random problems of the end-to-end test whose key blocks fit the fused kernel:
     equal to the unfused path bit for bit (partial strips, both policies, D = 64 and 128)."""
@@ -657,33 +727,115 @@ def test_step_captured_in_a_graph_replays_exactly():
 
 # ---------------------------------------------------------------- full size (sampled)
 
-@pytest.mark.slow
-@pytest.mark.parametrize("cfg,rho", [(I.S720P, 0.2), (I.SWEEP[0], 0.2), (I.S720P_B64, 0.2), (I.S720P_B256, 0.2)],
-                         ids=lambda x: getattr(x, "name", str(x)))
-def test_full_size_sampled(cfg, rho):
-    """The timed launch configuration at full size: selection on every row of sampled heads,
-    attention on sampled query blocks (first, last partial, random); also the 720p scale at
-    the block sizes 64 and 256 of the pages' ablation."""
-    print_case("full size", cfg.name, rho)
+_SCORES = {}
+
+
+def _oracle_scores(cfg, Q, K, h):
+    """Float64 oracle block scores of one head (kept across the densities of one workload)."""
+    if any(key[0] != cfg.name for key in _SCORES):
+        _SCORES.clear()
+    if (cfg.name, h) not in _SCORES:
+        b = cfg.block
+        _SCORES[(cfg.name, h)] = O.block_scores(O.pool_blocks(head_np(Q, h), b), O.pool_blocks(head_np(K, h), b),
+                                                cfg.softmax_scale)
+    return _SCORES[(cfg.name, h)]
+
+
+def _full_size_check(cfg, rho, rows_per_head, heads=None):
+    """The timed launch configuration at full size, against the oracle:
+    * selection on every row of every head (near-tie rule);
+    * attention on `rows_per_head` query blocks of every head (first, last partial, seeded random),
+      the oracle fed the GPU's own block lists, for the bf16-stored output that the benchmark times
+      (max-abs beyond the store's own rounding) and for the float32-stored output of the same kernel
+      on the same lists (the plain max-abs 1e-2 / mean-abs 1e-3 gate)."""
     Q, K, V = inputs(cfg)
-    (out, lse), (sc, rp, ci) = S.scale_forward(Q, K, V, scale_of(cfg), rho, return_lse=True)
+    sc = scale_of(cfg)
+    qp, kp, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, rho, cfg.policy)
+    out_bf, lse = S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, return_lse=True)
+    out_f32 = S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, out_dtype=torch.float32)
     torch.cuda.synchronize()
+    assert out_bf.dtype == torch.bfloat16
     lists = csr_rows(rp, ci)
     b = cfg.block
     nq = O.num_blocks(cfg.len_q, b)
-    heads = [0, cfg.heads - 1]
+    R, C = O.retained_and_candidates(cfg.len_text, cfg.len_ref, cfg.len_q, b, cfg.policy)
+    kk = O.budget(len(C), rho)
+    heads = range(cfg.heads) if heads is None else heads
     swaps = 0
     for h in heads:
-        q, k = head_np(Q, h), head_np(K, h)
-        S_ref = O.block_scores(O.pool_blocks(q, b), O.pool_blocks(k, b), cfg.softmax_scale)
-        R, C = O.retained_and_candidates(cfg.len_text, cfg.len_ref, cfg.len_q, b)
-        kk = O.budget(len(C), rho)
+        S_ref = _oracle_scores(cfg, Q, K, h)
         ref_sets = O.select_blocks(S_ref, R, C, kk)
         for i in range(nq):
             swaps += compare_row_selection(lists[h * nq + i], ref_sets[i], S_ref[i], len(R), kk)
-    print(f"near-tie swaps over {len(heads) * nq} rows: {swaps}")
+    print(f"{cfg.name} rho {rho}: selection on {len(heads) * nq} rows, {swaps} near-tie swaps")
 
     def sampler(h):
         rng = np.random.default_rng(100 + h)
-        return sorted({0, nq - 1, *rng.choice(nq, 4, replace=False).tolist()})
-    _check_attention(cfg, Q, K, V, lists, out, lse, [0, 13, cfg.heads - 1], sampler, True)
+        pick = rng.choice(np.arange(1, nq - 1), rows_per_head - 2, replace=False).tolist()
+        return sorted({0, nq - 1, *pick})
+    mx_bf, mean_bf = _check_attention(cfg, Q, K, V, lists, out_bf, lse, list(heads), sampler, True)
+    mx_32, mean_32 = _check_attention(cfg, Q, K, V, lists, out_f32, None, list(heads), sampler, True)
+    print(f"{cfg.name} rho {rho}: raw max-abs bf16-stored {mx_bf:.3e} (mean {mean_bf:.3e}), "
+          f"float32-stored {mx_32:.3e} (mean {mean_32:.3e})")
+    return out_bf, rp, ci
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("rho", [0.1, 0.2, 0.4])
+def test_full_size_720p(rho):
+    """The 72,000-token 720p final scale at each sparse density: every head, every row's selection,
+    32 heads x 16 query blocks of attention, bf16- and float32-stored output."""
+    print_case("full size 720p", rho)
+    _full_size_check(I.S720P, rho, 16)
+
+
+@pytest.mark.slow
+def test_full_size_720p_dense():
+    """Density 1 at 720p: dense_attn_fwd against the oracle's plain softmax over every key
+    (32 heads x 4 query blocks: first, last partial, two seeded), both output dtypes; the selection
+    at density 1 lists every block, and the sparse kernel over it equals the dense one bit for bit."""
+    cfg = I.S720P
+    print_case("full size 720p dense")
+    Q, K, V = inputs(cfg)
+    sc = scale_of(cfg)
+    d_bf, lse = S.dense_attn_fwd(Q, K, V, sc, return_lse=True)
+    d_32 = S.dense_attn_fwd(Q, K, V, sc, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    nq, nk = O.num_blocks(cfg.len_q, cfg.block), O.num_blocks(cfg.len_k, cfg.block)
+    lists = [np.arange(nk)] * (nq * cfg.heads)
+
+    def sampler(h):
+        rng = np.random.default_rng(7 + h)
+        return sorted({0, nq - 1, *rng.choice(np.arange(1, nq - 1), 2, replace=False).tolist()})
+    mx_bf, _ = _check_attention(cfg, Q, K, V, lists, d_bf, lse, range(cfg.heads), sampler, True)
+    mx_32, _ = _check_attention(cfg, Q, K, V, lists, d_32, None, range(cfg.heads), sampler, True)
+    print(f"dense 720p: raw max-abs bf16-stored {mx_bf:.3e}, float32-stored {mx_32:.3e}")
+    _, _, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, 1.0)
+    a = S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc)
+    torch.cuda.synchronize()
+    assert int(rp[-1]) == cfg.heads * nq * nk
+    assert torch.equal(ci.view(cfg.heads * nq, nk).cpu(),
+                       torch.arange(nk, dtype=torch.int32).repeat(cfg.heads * nq, 1))
+    assert torch.equal(a, d_bf)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_full_size_sweep(idx):
+    """The four scales of the 720p clip-pyramid sweep (per-scale seeds; scales 1 and 2 have their own
+    partial last query and key blocks), each with fresh selection at density 0.2: every head, every
+    row's selection, 32 heads x 16 query blocks of attention, both output dtypes."""
+    cfg = I.SWEEP[idx]
+    print_case("full size sweep", cfg.name)
+    _full_size_check(cfg, 0.2, 16)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [I.S720P_B64, I.S720P_B256], ids=lambda x: x.name)
+def test_full_size_block_sizes(cfg):
+    """The 720p scale at the block sizes 64 and 256 of the pages' ablation: selection on every row of
+    four heads, attention on 6 query blocks of each, both output dtypes."""
+    print_case("full size", cfg.name)
+    _full_size_check(cfg, 0.2, 6, heads=[0, 11, 20, cfg.heads - 1])
