@@ -250,6 +250,35 @@ sparstar_status bsa_fwd_balanced_impl(const sparstar_problem* p, const void* q, 
   return run_attn(p, a, counters, stream);
 }
 
+
+// Library-held scratch for sparstar_bsa_fwd_balanced_noalloc: the row-queue counters
+// and the row order of the balanced call, for callers that cannot allocate.  Each
+// device holds its own copy of the array until the process ends.  In host code
+// `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchBytes = int64_t(1) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+sparstar_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPARSTAR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPARSTAR_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(SPARSTAR_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                hipGetErrorString(g_scratch_err[dev]));
+  *ptr = g_scratch_ptr[dev];
+  return SPARSTAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -613,6 +642,28 @@ sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void*
   return guarded([&]() -> sparstar_status {
     if (!workspace) return fail(SPARSTAR_ERR_NULL, "workspace must be non-NULL");
     return bsa_fwd_balanced_impl(p, q, k, v, row_ptr, col_idx, col_idx_len, out, lse, workspace, workspace_bytes,
+                                 (hipStream_t)stream);
+  });
+}
+
+sparstar_status sparstar_bsa_fwd_balanced_noalloc(const sparstar_problem* p, const void* q, const void* k,
+                                                  const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                                                  int64_t col_idx_len, void* out, float* lse, void* stream) {
+  return guarded([&]() -> sparstar_status {
+    sparstar_status s = check_problem_impl(p);
+    if (s != SPARSTAR_OK) return s;
+    const int64_t need = balance_workspace_bytes(p);
+    if (need > kScratchBytes)
+      return fail(SPARSTAR_ERR_CAPACITY,
+                  "the problem needs %lld bytes of row queue and order; the library's scratch holds %lld "
+                  "(use sparstar_bsa_fwd_balanced with a workspace)",
+                  (long long)need, (long long)kScratchBytes);
+    void* ws = nullptr;
+    if ((int64_t)p->batch * p->heads * ceil_div(p->len_q, p->block) > 0) {
+      if ((s = check_device()) != SPARSTAR_OK) return s;
+      if ((s = scratch_on_current_device(&ws)) != SPARSTAR_OK) return s;
+    }
+    return bsa_fwd_balanced_impl(p, q, k, v, row_ptr, col_idx, col_idx_len, out, lse, ws, kScratchBytes,
                                  (hipStream_t)stream);
   });
 }

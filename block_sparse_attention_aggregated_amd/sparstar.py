@@ -73,6 +73,8 @@ _SIGS = {
     "sparstar_attention_kernel": (_c_i32, [ctypes.POINTER(Problem)]),
     "sparstar_bsa_fwd_balanced": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
                                            _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "sparstar_bsa_fwd_balanced_noalloc": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                   _c_i64, _c_vp, _c_vp, _c_vp]),
     "sparstar_block_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "sparstar_selection_mass": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]),
     "sparstar_window_scores": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp]),
@@ -343,6 +345,24 @@ def sparstar_bsa_fwd_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                            _ptr(col_idx), col_idx.numel(), _ptr(out), _ptr(lse), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(q.device)))
     return (out, lse) if return_lse else out
+
+
+def sparstar_bsa_fwd_balanced_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                                      col_idx: torch.Tensor, scale: Scale, out: torch.Tensor,
+                                      lse: Optional[torch.Tensor] = None) -> None:
+    """sparstar_bsa_fwd_balanced with the library's own scratch: the caller passes every output."""
+    p = problem(q, k, v, scale, out=out)
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise SparstarError(ERR_UNSUPPORTED, "row_ptr and col_idx must be int32")
+    rows = q.shape[0] * q.shape[1] * num_q_blocks(p)
+    if row_ptr.numel() != rows + 1 or not row_ptr.is_contiguous() or not col_idx.is_contiguous():
+        raise SparstarError(ERR_SHAPE, f"row_ptr must hold {rows + 1} entries, contiguous")
+    if lse is not None and (tuple(lse.shape) != tuple(q.shape[:3]) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise SparstarError(ERR_SHAPE, "lse must be contiguous float32 [B, H, L_q]")
+    _check(lib().sparstar_bsa_fwd_balanced_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                                   _ptr(col_idx), col_idx.numel(), _ptr(out), _ptr(lse),
+                                                   _stream(q.device)))
 
 
 def dense_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Scale, out=None,

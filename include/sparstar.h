@@ -246,6 +246,24 @@ sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void*
                                           int64_t col_idx_len, void* out, float* lse, void* workspace,
                                           int64_t workspace_bytes, void* stream);
 
+/* sparstar_bsa_fwd_balanced without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The row queues' counters and the row order
+ * live in a scratch array the library holds on each device (1 MiB, kept until the
+ * process ends; its address is looked up once per device, on the first call there);
+ * the call allocates nothing.  Problems whose queues and order need more than that
+ * (sparstar_balance_workspace_bytes > 1,048,576, i.e. B*H*S*ceil(n_q/S) above 262,080
+ * rows) are refused with SPARSTAR_ERR_CAPACITY before anything is enqueued.  Every
+ * call on one device shares that device's scratch, which keeps the last call's
+ * contents (the call clears the counters itself): calls that overlap on one device,
+ * on different streams or from different threads, race and must not be made.
+ * Arguments, results and errors otherwise as sparstar_bsa_fwd_balanced; the outputs
+ * are the same, bit for bit. */
+sparstar_status sparstar_bsa_fwd_balanced_noalloc(const sparstar_problem* p, const void* q, const void* k,
+                                                  const void* v, const int32_t* row_ptr,
+                                                  const int32_t* col_idx, int64_t col_idx_len, void* out,
+                                                  float* lse, void* stream);
+
 /* ---------------- retained attention mass (the pages' quality measure of a selection) ---
  * Section 4 "Analysis" (Figure 3; "Pattern Persistence across Clip Boundaries")
  * and section 1 measure a selection by the share of each query's dense softmax

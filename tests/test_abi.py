@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 23
+    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 24
     assert {"sparstar_pool_blocks", "sparstar_score_select"} <= set(names)
     assert {"sparstar_block_mass", "sparstar_selection_mass", "sparstar_window_scores",
             "sparstar_token_topk_mass"} <= set(names)
@@ -235,6 +235,23 @@ def test_too_many_candidates_is_refused():
     b = ctypes.c_void_p(BOGUS)
     st = S.lib().sparstar_select_blocks(ctypes.byref(p), b, 0.2, 0, b, b, 10**12, None)
     assert st == S.ERR_UNSUPPORTED
+
+
+@no_gpu
+def test_noalloc_refuses_problems_beyond_its_scratch():
+    """The allocation-free call holds 1 MiB of queue counters and row order per device: a problem whose
+    order does not fit is refused before anything touches a device, with a message saying why."""
+    L = S.lib()
+    b = ctypes.c_void_p(BOGUS)
+    p = _prob(I.S720P)
+    assert 256 + 4 * 32 * 4 * 141 <= 1 << 20
+    big = _prob(I.S720P.with_(batch=16))                 # 16 * 32 heads * 4 segments * 141 rows
+    assert S.balance_workspace_bytes(big) > 1 << 20
+    st = L.sparstar_bsa_fwd_balanced_noalloc(ctypes.byref(big), b, b, b, b, b, 10, b, None, None)
+    assert st == S.ERR_CAPACITY and "scratch" in S.last_error()
+    assert L.sparstar_bsa_fwd_balanced_noalloc(None, b, b, b, b, b, 10, b, None, None) == S.ERR_NULL
+    assert L.sparstar_bsa_fwd_balanced_noalloc(ctypes.byref(p), b, b, b, None, b, 10, b, None, None) \
+        in (S.ERR_NULL, S.ERR_UNSUPPORTED, S.ERR_HIP)
 
 
 def test_attention_kernel_choice():
