@@ -126,49 +126,72 @@ def traffic_record():
     return rec if rec.get("kernel_sha256") == src else None
 
 
-def cpu_baseline(cfg, density, policy, Q, K, V, rows_per_head):
-    """Time the float64 oracle on a bounded sample of the scale: pooling, scoring and
-    selection of every head, and attention of rows_per_head query blocks per head
-    (first, last and seeded random ones); the attention time is extrapolated to all
-    rows by executed FLOPs.  About 10-20 s of CPU work at 720p."""
+def _oracle_head(job):
+    """One head of the CPU baseline, in a worker process: draw the head's inputs from the seeded
+    generator (the same values the GPU got; not timed), then time the float64 oracle's pooling,
+    scoring and selection, and its attention on the sampled query blocks."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    from block_sparse_attention_aggregated_amd import inputs as I
+    cfg, h, density, policy, rows = job
+    q, k, v = I.head_f64(cfg, h)
     b, sigma = cfg.block, cfg.softmax_scale
+    t0 = time.perf_counter()
+    res = O.scale_head(q, k, v, cfg.len_text, cfg.len_ref, b, sigma, density, policy, rows=[])
+    t_sel = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.sparse_attention(q, k, v, res["sets"], b, sigma, rows=rows)
+    t_att = time.perf_counter() - t0
+    nq = O.num_blocks(cfg.len_q, b)
+    flops_rows = O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim,
+                                  [res["sets"][i] if i in rows else [] for i in range(nq)])
+    flops_all = O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim, res["sets"])
+    return t_sel, t_att, flops_rows, flops_all
+
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def cpu_baseline(cfg, density, policy, rows_per_head):
+    """Time the float64 oracle on a bounded sample of the scale, one head per task on a pool of
+    worker processes (one per available core, at most 16; one BLAS thread each): pooling, scoring
+    and selection of every head, and attention of rows_per_head query blocks per head (first, last
+    and seeded random ones).  The attention time is extrapolated to all rows by executed FLOPs, and
+    the per-head times, taken while the workers run side by side, are summed and divided by the
+    worker count (the heads are independent and evenly spread).  About 10-30 s of CPU work at 720p."""
+    import multiprocessing as mp
+
+    import oracle as O
+    b = cfg.block
     nq = O.num_blocks(cfg.len_q, b)
     rng = np.random.default_rng(0)
-    t_sel = t_att = 0.0
-    flops_rows = flops_all = 0
-    n_rows = 0
-    for bi in range(cfg.batch):
-        for h in range(cfg.heads):
-            q = Q[bi, h].cpu().double().numpy()
-            k = K[bi, h].cpu().double().numpy()
-            v = V[bi, h].cpu().double().numpy()
-            t0 = time.perf_counter()
-            res = O.scale_head(q, k, v, cfg.len_text, cfg.len_ref, b, sigma, density, policy, rows=[])
-            t_sel += time.perf_counter() - t0
-            pick = rng.choice(nq, max(0, min(nq, rows_per_head) - 2), replace=False).tolist()
-            rows = sorted({0, nq - 1, *pick})[:max(rows_per_head, 1)]
-            t0 = time.perf_counter()
-            O.sparse_attention(q, k, v, res["sets"], b, sigma, rows=rows)
-            t_att += time.perf_counter() - t0
-            n_rows += len(rows)
-            flops_rows += O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim,
-                                           [res["sets"][i] if i in rows else [] for i in range(nq)])
-            flops_all += O.executed_flops(cfg.len_q, cfg.len_k, b, cfg.head_dim, res["sets"])
-    t_total = t_sel + t_att * flops_all / max(flops_rows, 1)
+    jobs = []
+    for h in range(cfg.heads):
+        pick = rng.choice(nq, max(0, min(nq, rows_per_head) - 2), replace=False).tolist()
+        jobs.append((cfg, h, density, policy, sorted({0, nq - 1, *pick})[:max(rows_per_head, 1)]))
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(jobs)))
+    with mp.get_context("spawn").Pool(workers, initializer=_one_blas_thread) as pool:
+        res = pool.map(_oracle_head, jobs, chunksize=1)
+    t_sel = sum(r[0] for r in res)
+    t_att = sum(r[1] for r in res)
+    flops_rows = sum(r[2] for r in res)
+    flops_all = sum(r[3] for r in res)
+    n_rows = sum(len(j[4]) for j in jobs)
+    t_total = (t_sel + t_att * flops_all / max(flops_rows, 1)) / workers
     return {
-        "value": flops_all / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "value": float(flops_all / t_total / 1e12), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
         "cpu_model": cpu_model(), "host_cpus_available": len(os.sched_getaffinity(0)),
-        "ms_per_scale_extrapolated": t_total * 1e3,
-        "sample": (f"float64 numpy oracle on the same inputs: pooling+scoring+selection of all "
-                   f"{cfg.batch * cfg.heads} heads ({t_sel:.1f} s) and attention of {n_rows} of "
-                   f"{cfg.batch * cfg.heads * nq} query blocks ({rows_per_head} per head: first, last, "
-                   f"seeded random; {t_att:.1f} s), attention extrapolated to all rows by executed FLOPs"),
+        "ms_per_scale_extrapolated": float(t_total * 1e3),
+        "sample": (f"float64 numpy oracle, one head per task on {workers} worker processes with one BLAS "
+                   f"thread each, inputs drawn from the same seeded generator: pooling+scoring+selection of "
+                   f"all {cfg.batch * cfg.heads} heads ({t_sel:.1f} s of worker time) and attention of {n_rows} of "
+                   f"{cfg.batch * cfg.heads * nq} query blocks ({rows_per_head} per head: first, last, seeded "
+                   f"random; {t_att:.1f} s), attention extrapolated to all rows by executed FLOPs, worker time "
+                   f"divided by the worker count"),
     }
 
 
@@ -347,10 +370,18 @@ def time_calls(fns, reps, warmup, flush=None):
 
 
 def infinity_cache_flush(dev, mb=512):
-    """A callable that writes `mb` MiB of scratch, evicting the Infinity Cache (256 MB) and L2."""
+    """A callable that evicts the Infinity Cache (256 MB) and the L2s: it writes `mb` MiB of scratch
+    and then reads it back (a sum), so the caches end up holding clean lines of the scratch buffer
+    and the timed kernel that follows neither hits on its inputs nor pays for writing back the
+    flush's dirty lines."""
     import torch
     buf = torch.empty((mb << 20) // 4, dtype=torch.float32, device=dev)
-    return lambda: buf.fill_(1.0)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        buf.fill_(1.0)
+        torch.sum(buf, dim=0, out=out)
+    return flush
 
 
 def scale_report(cfg, density, dev, reps=5, warmup=2, dense=False, inputs=None, flush=None):
@@ -432,7 +463,7 @@ def north_star_report(dev, q720=None, log=lambda m: None):
         "dense_over_sparse_720p_rho0.1": {"operator": dense["ms_attention"] / r01["ms_attention"],
                                           "step": dense["ms_attention"] / r01["ms_scale"]},
         "timing": "HIP events on the launch stream; 5 timed reps after 2 warm-up (dense: 3 after 1); "
-                  "pool_score timed after a 512 MiB scratch write that evicts the Infinity Cache",
+                  "pool_score timed after a 512 MiB scratch write and read-back that evict the Infinity Cache",
     }
 
 
@@ -622,8 +653,7 @@ def main():
     if not args.no_cpu_baseline and not args.dense and not args.uneven:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         s = scales[-1]
-        rec["cpu_baseline"] = cpu_baseline(s["cfg"], s["density"], s["policy"], s["Q"], s["K"], s["V"],
-                                           args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(s["cfg"], s["density"], s["policy"], args.cpu_rows)
         print(f"# oracle sample: {rec['cpu_baseline']['sample']}", file=sys.stderr, flush=True)
     line = json.dumps(rec)
     print(line, flush=True)

@@ -59,3 +59,11 @@ def test_uneven_lists_recipe():
     assert order[:8].tolist() == [0, 2, 4, 6, 8, 10, 12, 14]
     order = bench.dispatch_order(1, 3, 16, 128)
     assert order[:8].tolist() == [0, 2, 4, 6, 8, 10, 12, 14]
+
+
+def test_cache_flush_and_cpu_model_helpers():
+    sys.path.insert(0, ROOT)
+    import bench
+    flush = bench.infinity_cache_flush("cpu", mb=4)
+    flush()
+    assert isinstance(bench.cpu_model(), str)
