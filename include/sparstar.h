@@ -186,11 +186,13 @@ int64_t sparstar_bsa_workspace_bytes(const sparstar_problem* p);
  *              owned by the caller (SPARSTAR_ERR_CAPACITY if smaller).  With it, a
  *              persistent grid of as many workgroups as fit on the GPU at once takes
  *              the rows from per-XCD queues with atomic counters, which the call
- *              clears itself (a kernel, no memset), and a workgroup whose XCD has no
+ *              sets itself (a kernel, no memset), and a workgroup whose XCD has no
  *              rows left takes rows from the other XCDs' queues; two calls must not
  *              share a workspace while either runs.  With NULL (and any
- *              workspace_bytes), one workgroup per row, handed to the XCDs by the
- *              hardware dispatcher.  The outputs are the same, bit for bit, either way.
+ *              workspace_bytes), or when the problem has fewer rows than two
+ *              rounds of the persistent grid per XCD, one workgroup per row, handed
+ *              to the XCDs by the hardware dispatcher (the workspace is then not
+ *              touched).  The outputs are the same, bit for bit, either way.
  * bf16 inputs with D = 128 run on bf16 MFMA with float32 softmax and accumulation
  * for every block size (64, 128, 256: the block sizes of appendix D.2 "Block-Size
  * Ablation").
@@ -233,7 +235,7 @@ int64_t sparstar_balance_workspace_bytes(const sparstar_problem* p);
  * atomic counters: a workgroup whose XCD's queue is empty takes rows from the other
  * XCDs' queues, so no XCD idles while another still has rows.  `workspace` is a device
  * buffer of at least sparstar_balance_workspace_bytes, owned by the caller; the call
- * clears the counters itself (a kernel, no memset).  On return bytes [0, 256) hold the
+ * sets the counters itself (a kernel, no memset).  On return bytes [0, 256) hold the
  * counters and from byte 256 on the order: entry (b*H + h)*S*ceil(n_q/S) + x*ceil(n_q/S) + m
  * is the query block of the m-th row of segment x, -1 past the segment's end.  Every row
  * is computed exactly as by sparstar_bsa_fwd: the outputs are the same, bit for bit.  The
@@ -255,7 +257,7 @@ sparstar_status sparstar_bsa_fwd_balanced(const sparstar_problem* p, const void*
  * (sparstar_balance_workspace_bytes > 1,048,576, i.e. B*H*S*ceil(n_q/S) above 262,080
  * rows) are refused with SPARSTAR_ERR_CAPACITY before anything is enqueued.  Every
  * call on one device shares that device's scratch, which keeps the last call's
- * contents (the call clears the counters itself): calls that overlap on one device,
+ * contents (the call sets the counters itself): calls that overlap on one device,
  * on different streams or from different threads, race and must not be made.
  * Arguments, results and errors otherwise as sparstar_bsa_fwd_balanced; the outputs
  * are the same, bit for bit. */

@@ -335,15 +335,17 @@ def test_irregular_csr(D, b, dtype):
             assert np.max(np.abs(got_l[s:e] - l_ref)) < LSE_BF16
 
 
-@pytest.mark.parametrize("D,b,dtype,H", [(128, 128, torch.bfloat16, 3), (128, 64, torch.bfloat16, 3),
-                                         (128, 256, torch.bfloat16, 3), (64, 64, torch.float32, 3),
-                                         (128, 128, torch.bfloat16, 2), (128, 256, torch.bfloat16, 4)])
-def test_balanced_equals_plain_bitwise(D, b, dtype, H):
+@pytest.mark.parametrize("D,b,dtype,H,L_q", [(128, 128, torch.bfloat16, 3, 1000), (128, 64, torch.bfloat16, 3, 1000),
+                                             (128, 256, torch.bfloat16, 3, 1000), (64, 64, torch.float32, 3, 1000),
+                                             (128, 128, torch.bfloat16, 2, 1000), (128, 256, torch.bfloat16, 4, 1000),
+                                             (128, 128, torch.bfloat16, 16, 16384)])
+def test_balanced_equals_plain_bitwise(D, b, dtype, H, L_q):
     """Rows started longest list first give the same outputs, bit for bit, as the plain call:
     uneven random lists plus the irregular kinds (empty, duplicates, out of range); odd head
-    counts use 8 segments per head, even ones at b = 128 and 256 use 4."""
-    L_text, L_ref, L_q = 64, 900, 1000
-    print_case("balanced", D, b, dtype, H)
+    counts use 8 segments per head, even ones at b = 128 and 256 use 4.  The 16-head problem has
+    enough rows for the persistent queues; the small ones run one workgroup per row."""
+    L_text, L_ref = 64, 900
+    print_case("balanced", D, b, dtype, H, L_q)
     Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, D, dtype, seed=12)
     scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(D))
     nq, nk = O.num_blocks(L_q, b), O.num_blocks(L_text + L_ref + L_q, b)
@@ -387,15 +389,23 @@ def test_balanced_equals_plain_bitwise(D, b, dtype, H):
 def test_static_and_dynamic_queues_bitwise(b):
     """The two ways of handing out rows (one workgroup per row without a workspace, a persistent grid
     on per-XCD atomic queues with one) compute every row the same way: equal bit for bit, on the
-    selection's lists, on irregular ones (empty rows, duplicates, out-of-range entries) and dense."""
-    L_text, L_ref, L_q, H = 64, 700, 900, 3
+    selection's lists, on irregular ones (empty rows, duplicates, out-of-range entries) and dense.
+    The problem has enough rows for the queues (at least two rounds of resident workgroups per XCD);
+    the counters left in the workspace show which way ran: a smaller problem, with fewer rows than
+    that, runs one workgroup per row even with a workspace and leaves the counters alone."""
+    L_text, L_ref, L_q, H = 64, 1000, 16384, 16
     print_case("static vs dynamic queues", b)
     Q, K, V = _custom_inputs(L_text, L_ref, L_q, H, 128, torch.bfloat16, seed=21)
     scale = S.Scale(L_text, L_ref, b, 1 / math.sqrt(128))
-    (a, la), (_, rp, ci) = S.scale_forward(Q, K, V, scale, 0.3, return_lse=True)
+    STALE = 12345
+    ws = torch.full((64,), STALE, dtype=torch.int32, device=DEV)          # stale counters: the call sets them
+    _, _, scores = S.sparstar_pool_score(Q, K, scale)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, scale, 0.3)
+    a, la = S.sparstar_bsa_fwd(Q, K, V, rp, ci, scale, return_lse=True, workspace=ws)
     c, lc = S.sparstar_bsa_fwd(Q, K, V, rp, ci, scale, return_lse=True, workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(a, c) and torch.equal(la, lc)
+    assert not torch.all(ws[:8] == STALE), "the persistent queues did not run"
     nq, nk = O.num_blocks(L_q, b), O.num_blocks(L_text + L_ref + L_q, b)
     rng = np.random.default_rng(4)
     lists = [np.zeros(0, np.int64) if r % 5 == 0 else np.array([1, 1, -3, nk]) if r % 5 == 1
@@ -404,17 +414,27 @@ def test_static_and_dynamic_queues_bitwise(b):
     rp_np[1:] = np.cumsum([len(x) for x in lists])
     rp_t = torch.from_numpy(rp_np).to(DEV)
     ci_t = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(DEV)
-    ws = torch.full((64,), 12345, dtype=torch.int32, device=DEV)        # stale counters: the call clears them
+    ws.fill_(STALE)
     d, ld = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True, workspace=ws)
     e, le = S.sparstar_bsa_fwd(Q, K, V, rp_t, ci_t, scale, return_lse=True, workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(d, e) and torch.equal(ld, le)
+    assert not torch.all(ws[:8] == STALE)
     # the dense path: persistent queues and one workgroup per row
     ws.fill_(-5)
     f, lf = S.dense_attn_fwd(Q, K, V, scale, return_lse=True, workspace=ws)
     g, lg = S.dense_attn_fwd(Q, K, V, scale, return_lse=True, workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(f, g) and torch.equal(lf, lg)
+    assert not torch.all(ws[:8] == -5)
+    # too few rows for the queues: one workgroup per row, the counters untouched
+    Qs, Ks, Vs = Q[:, :2, :1024].contiguous(), K[:, :2, :L_text + L_ref + 1024].contiguous(), \
+        V[:, :2, :L_text + L_ref + 1024].contiguous()
+    ws.fill_(STALE)
+    h1 = S.dense_attn_fwd(Qs, Ks, Vs, scale, workspace=ws)
+    h2 = S.dense_attn_fwd(Qs, Ks, Vs, scale, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.all(ws == STALE)
 
 
 def test_balanced_on_the_selection():

@@ -36,7 +36,9 @@ def _problem(L_text, L_ref, L_q, H, b, seed, uneven):
 
 @pytest.mark.parametrize("uneven", [False, True])
 def test_noalloc_equals_balanced_on_two_calls(uneven):
-    cases = [(512, 3000, 3000, 4, 128, 31), (64, 700, 900, 2, 128, 32)]      # the second call is smaller
+    # the first problem has enough rows per XCD for the persistent queues, the second (smaller) one runs
+    # one workgroup per row
+    cases = [(512, 3000, 16384, 16, 128, 31), (64, 700, 900, 2, 128, 32)]
     for L_text, L_ref, L_q, H, b, seed in cases:
         print("CASE noalloc", L_text, L_ref, L_q, H, b, seed, "uneven" if uneven else "selection", flush=True)
         Q, K, V, scale, rp, ci = _problem(L_text, L_ref, L_q, H, b, seed, uneven)
