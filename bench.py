@@ -15,6 +15,9 @@ inputs already resident in HBM.  Prints one JSON line:
                HIP events on the stream the kernels run on
   cpu_baseline the float64 CPU oracle on a bounded sample of the same scale,
                extrapolated to the whole scale (a baseline, not a target)
+  sustained    steps run back to back for --sustain seconds with the board
+               power and the XCD clocks sampled through amd-smi, and the bf16
+               MFMA peak at the sampled clock
 
 --dense times dense_attn_fwd instead (the density-1 baseline); --mass measures
 the retained attention mass of the selection strategies and times the
@@ -81,6 +84,9 @@ def parse():
                          "token-wise Top-K bound with the block selections")
     ap.add_argument("--no-report", action="store_true",
                     help="skip the per-configuration report (192p, 480p, 720p at 0.1/0.2/0.4/1.0, sweep)")
+    ap.add_argument("--sustain", type=float, default=5.0,
+                    help="seconds of back-to-back steps after the timed ones, with the board power and the "
+                         "XCD clocks sampled through amd-smi (0: skip)")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -327,6 +333,94 @@ def uneven_lists(n_rows, n_k, r, k, seed=7, even=False, first=None):
     row_ptr = np.zeros(n_rows + 1, dtype=np.int64)
     row_ptr[1:] = np.cumsum([len(x) for x in rows])
     return row_ptr.astype(np.int32), np.concatenate(rows).astype(np.int32), counts
+
+
+def parse_smi(d):
+    """Socket power (W), the XCD clocks and the memory clock (MHz) of the first GPU in the JSON of
+    `amd-smi metric -p -c --json`; None when they are missing."""
+    vals = {}
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            if "value" in x and not isinstance(x["value"], (dict, list)):
+                vals[path] = x["value"]
+                return
+            for k, v in x.items():
+                walk(v, path + "/" + str(k).lower())
+        elif isinstance(x, list):
+            for i, v in enumerate(x[:1]):     # the first GPU: the one this process uses
+                walk(v, path + "/" + str(i))
+
+    def num(v):
+        try:
+            return float(v)
+        except (TypeError, ValueError):
+            return None
+
+    walk(d, "")
+    power = [num(v) for k, v in vals.items() if k.endswith("/socket_power")]
+    gfx = [num(v) for k, v in vals.items() if "/gfx_" in k and k.endswith("/clk")]
+    mem = [num(v) for k, v in vals.items() if "/mem_0/" in k and k.endswith("/clk")]
+    power, gfx, mem = ([x for x in a if x is not None] for a in (power, gfx, mem))
+    if not power or not gfx:
+        return None
+    return {"power_w": power[0], "gfx_mhz": gfx, "mem_mhz": mem[0] if mem else None}
+
+
+def _smi_sample():
+    """One amd-smi reading of the board power and clocks (None if amd-smi is unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=10)
+        return parse_smi(json.loads(r.stdout)) if r.returncode == 0 else None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+
+
+def sustained_run(step, seconds, flops, achieved_short):
+    """Steps back to back for `seconds`, with amd-smi sampled from a second thread.  Reports the
+    sustained time per step, the board power and the XCD clocks, and the bf16 MFMA peak at the
+    sampled clock (the published peak is quoted at 2.4 GHz)."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            r = _smi_sample()
+            if r is not None:
+                samples.append(r)
+            stop.wait(0.25)
+
+    step()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        n += 4
+    wall = time.perf_counter() - t0
+    stop.set()
+    th.join(timeout=15)
+    rec = {"seconds": wall, "steps": n, "ms_per_step": wall * 1e3 / n, "tflops": flops * n / wall / 1e12,
+           "smi_samples": len(samples), "source": "amd-smi metric -p -c --json"}
+    # Drop the readings of the first second (the clocks ramp up from idle).
+    busy = samples[len(samples) // max(1, int(seconds)):] if samples else []
+    if busy:
+        pw = [x["power_w"] for x in busy]
+        clk = [float(np.mean(x["gfx_mhz"])) for x in busy]
+        lo = min(min(x["gfx_mhz"]) for x in busy)
+        hi = max(max(x["gfx_mhz"]) for x in busy)
+        mhz = float(np.mean(clk))
+        rec.update({"socket_power_w": {"mean": float(np.mean(pw)), "max": float(max(pw))},
+                    "xcd_clock_mhz": {"mean": mhz, "min": lo, "max": hi},
+                    "mem_clock_mhz": busy[-1]["mem_mhz"],
+                    "bf16_peak_at_clock_tflops": PEAK_BF16_TFLOPS * mhz / 2400.0,
+                    "attention_frac_at_clock": achieved_short / (PEAK_BF16_TFLOPS * mhz / 2400.0)})
+    return rec
 
 
 def cpu_model() -> str:
@@ -635,6 +729,10 @@ def main():
                                    "achieved": p["scoring_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": p["scoring_gbs"] / PEAK_HBM_GBS,
                                    "bytes": scoring_bytes(cfgs[0])}
+    if args.sustain > 0 and not args.uneven:
+        print(f"# {args.sustain:.0f} s of back-to-back steps with power and clock sampling", file=sys.stderr,
+              flush=True)
+        rec["sustained"] = sustained_run(step, args.sustain, flops, achieved)
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

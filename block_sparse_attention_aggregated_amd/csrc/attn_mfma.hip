@@ -87,6 +87,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int HD = 128;            // head_dim
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kBig = 18446744073709551616.0f;  // 2^64: bound on a lane's P sum per sub-tile
+constexpr int kFragAhead = 2;      // MFMAs between an LDS operand read and its use
 
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -550,9 +551,10 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
       // and with none pending every LDS wait below counts only the LDS reads ahead
       // of it (lgkmcnt(n) rather than lgkmcnt(0)).  vmcnt and expcnt: no wait.
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      bf16x8 kf[3], vf[3];
-      kf[0] = k_frag(k_nxt, 0, 0);
-      kf[1] = k_frag(k_nxt, 1 % NT, 1 / NT);
+      constexpr int AH = kFragAhead, RING = kFragAhead + 1;
+      bf16x8 kf[RING], vf[RING];
+#pragma unroll
+      for (int j = 0; j < AH; ++j) kf[j] = k_frag(k_nxt, j % NT, j / NT);
       PTile pu;
       float rs0 = 0.f, rs1 = 0.f, le_t = 0.f;
       // The softmax of pair i runs in three stages over three iterations (FMA in
@@ -574,10 +576,10 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
       f32x2 x_1 = st_a(1), e_0 = st_b(st_a(0));
 #pragma unroll
       for (int i = 0; i < N1; ++i) {
-        if (i + 2 < N1) kf[(i + 2) % 3] = k_frag(k_nxt, (i + 2) % NT, (i + 2) / NT);
-        else vf[i - (N1 - 2)] = v_frag(v_cur, i - (N1 - 2), 0);
+        if (i + AH < N1) kf[(i + AH) % RING] = k_frag(k_nxt, (i + AH) % NT, (i + AH) / NT);
+        else vf[i + AH - N1] = v_frag(v_cur, (i + AH - N1) & 3, (i + AH - N1) >> 2);
         const int kt = i % NT, ks = i / NT;
-        s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], ks == 0 ? f32x16{} : s_nxt[kt], 0,
+        s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % RING], qf[ks], ks == 0 ? f32x16{} : s_nxt[kt], 0,
                                                             0, 0);
         const f32x2 x_2 = i + 2 < N1 ? st_a(i + 2) : f32x2{};
         const f32x2 e_1 = i + 1 < N1 ? st_b(x_1) : f32x2{};
@@ -617,9 +619,9 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
       // Phase 2.  MFMA i: feature tile i & 3, key step i >> 2.
 #pragma unroll
       for (int i = 0; i < N2; ++i) {
-        if (i + 2 < N2) vf[(i + 2) % 3] = v_frag(v_cur, (i + 2) & 3, (i + 2) >> 2);
+        if (i + AH < N2) vf[(i + AH) % RING] = v_frag(v_cur, (i + AH) & 3, (i + AH) >> 2);
         const int dt = i & 3, ks = i >> 2;
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pu.v[ks], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % RING], pu.v[ks], o[dt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 

@@ -67,3 +67,19 @@ def test_cache_flush_and_cpu_model_helpers():
     flush = bench.infinity_cache_flush("cpu", mb=4)
     flush()
     assert isinstance(bench.cpu_model(), str)
+
+
+def test_parse_smi_reads_power_and_xcd_clocks():
+    sys.path.insert(0, ROOT)
+    import bench
+    clk = lambda v: {"clk": {"value": v, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                     "max_clk": {"value": 2400, "unit": "MHz"}, "clk_locked": "N/A"}
+    gpu = {"gpu": 0, "power": {"socket_power": {"value": 1390, "unit": "W"}, "gfx_voltage": "N/A"},
+           "clock": {**{f"gfx_{i}": clk(1500 + 10 * i) for i in range(8)}, "mem_0": clk(2000),
+                     "vclk_0": clk(59)}}
+    other = {"gpu": 1, "power": {"socket_power": {"value": 200, "unit": "W"}}, "clock": {"gfx_0": clk(100)}}
+    r = bench.parse_smi({"gpu_data": [gpu, other]})
+    assert r["power_w"] == 1390
+    assert r["gfx_mhz"] == [1500 + 10 * i for i in range(8)]
+    assert r["mem_mhz"] == 2000
+    assert bench.parse_smi({"gpu_data": [{"gpu": 0, "power": "N/A"}]}) is None
