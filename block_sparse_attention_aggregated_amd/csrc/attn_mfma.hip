@@ -74,6 +74,7 @@
 #include "sparstar_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace sparstar {
@@ -676,19 +677,24 @@ __global__ __launch_bounds__(Shape<kB>::kThreads, Shape<kB>::kWavesPerSimd) void
   }
 }
 
-// Workgroups per XCD that fit at once: CUs per XCD times workgroups per CU.
+// Workgroups per XCD that fit at once on the current device: CUs per XCD times
+// workgroups per CU (kept per device once known; 0 on failure).
 template <int kB, bool kDense, bool kOutBf16, bool kLse>
 int resident_per_xcd() {
-  static int cached = [] {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_kernel<kB, kDense, kOutBf16, kLse>,
-                                                     Shape<kB>::kThreads, 0) != hipSuccess)
-      return 0;
-    return (cus / kXcds) * per_cu;
-  }();
-  return cached;
+  constexpr int kDevices = 64;
+  static std::atomic<int> known[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
+  const int v = known[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_kernel<kB, kDense, kOutBf16, kLse>,
+                                                   Shape<kB>::kThreads, 0) != hipSuccess)
+    return 0;
+  const int r = (cus / kXcds) * per_cu;
+  if (r > 0) known[dev].store(r, std::memory_order_relaxed);
+  return r;
 }
 
 // Queue counters at launch: the first `taken` items of every queue are the

@@ -7,12 +7,16 @@
 // Retained and Selectable Blocks" (the retained prefix plus the k best
 // candidates of each row).
 //
-// One workgroup of 8 wavefronts per (batch * head, strip of 32 query blocks):
+// One workgroup of 16 wavefronts per (batch * head, strip of 32 query blocks):
 //   1. the strip's scores against every key block, 32 x 32 tiles on the float32
 //      matrix cores (v_mfma_f32_32x32x2_f32), written to LDS as order-preserving
-//      uint32 keys [32][n_k]; wavefront w computes key tiles w, w + 8, ...;
-//   2. wavefront w ranks the strip's rows w, w + 8, w + 16, w + 24 from LDS with
-//      the shared row selector.
+//      uint32 keys [32][n_k]; wavefront w computes key tiles w, w + 16, ...;
+//   2. wavefront w ranks the strip's rows w and w + 16 from LDS with the shared
+//      row selector.
+// The strip's keys fill nearly all of the LDS, so one workgroup runs per CU; 16
+// wavefronts (four per SIMD, 110 VGPRs each) hide more of the latency of the
+// pooled-row loads and of the selector's LDS atomics than 8 (0.20 against
+// 0.23 ms at 720p).
 // Each tile runs the score kernel's MFMA sequence: for feature chunk c (32
 // features), step q (4 features) and element e, lane l supplies feature
 // 32 c + 16 (l >> 5) + 4 q + e of query row l & 31 and of key row l & 31, and
@@ -27,7 +31,7 @@
 namespace sparstar {
 namespace {
 
-constexpr int kFWaves = 8;
+constexpr int kFWaves = 16;
 constexpr int kStrip = 32;
 constexpr int kHistWords = kFWaves * 256;
 constexpr int kKeyWords = (160 * 1024 - kHistWords * 4) / 4;  // LDS words left for keys

@@ -144,7 +144,7 @@ sparstar_status sparstar_pool_blocks(const sparstar_problem* p, const void* q, c
  *   q_pool, k_pool : in, float32 [B, H, n_q, D] / [B, H, n_k, D] contiguous
  *                    (sparstar_pool_blocks or sparstar_pool_score).
  *   density, policy, row_ptr, col_idx, col_idx_capacity : as sparstar_select_blocks.
- * A strip's scores must fit LDS: n_k at most 1,216 (SPARSTAR_ERR_UNSUPPORTED beyond). */
+ * A strip's scores must fit LDS: n_k at most 1,152 (SPARSTAR_ERR_UNSUPPORTED beyond). */
 sparstar_status sparstar_score_select(const sparstar_problem* p, const float* q_pool, const float* k_pool,
                                       double density, int32_t policy, int32_t* row_ptr, int32_t* col_idx,
                                       int64_t col_idx_capacity, void* stream);

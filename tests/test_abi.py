@@ -184,10 +184,10 @@ def test_fused_select_entry_points_validate_before_any_device_call():
     assert L.sparstar_score_select(ctypes.byref(p), None, b, 0.3, 0, b, b, nnz, None) == S.ERR_NULL
     assert L.sparstar_score_select(ctypes.byref(p), odd, b, 0.3, 0, b, b, nnz, None) == S.ERR_LAYOUT
     assert L.sparstar_score_select(ctypes.byref(p), b, b, 0.3, 0, b, b, nnz - 1, None) == S.ERR_CAPACITY
-    # a strip's scores must fit LDS: 1,216 key blocks at most
+    # a strip's scores must fit LDS: 1,152 key blocks at most
     big = _prob(I.S720P.with_(block=64))                                        # n_k = 2,258
     st = L.sparstar_score_select(ctypes.byref(big), b, b, 0.2, 0, b, b, 10**9, None)
-    assert st == S.ERR_UNSUPPORTED and "1216" in S.last_error()
+    assert st == S.ERR_UNSUPPORTED and "1152" in S.last_error()
 
 
 @no_gpu
