@@ -518,7 +518,7 @@ def scale_report(cfg, density, dev, reps=5, warmup=2, dense=False, inputs=None, 
     return rec
 
 
-def north_star_report(dev, q720=None, log=lambda m: None):
+def config_report(dev, q720=None, log=lambda m: None):
     """ms per scale, effective TFLOP/s and the fraction of the bf16 MFMA peak on every configuration:
     192p (0.3), 480p (0.25), 720p at 0.1, 0.2, 0.4 and 1.0 (dense), the four-scale 720p sweep (0.2
     each), and dense over sparse at 720p, density 0.1 (the analog of the pages' operator speed-up)."""
@@ -747,7 +747,7 @@ def main():
         def log(m):
             print(f"# {m}", file=sys.stderr, flush=True)
         s = scales[0]
-        rec["north_star_report"] = north_star_report(dev, q720=(s["Q"], s["K"], s["V"]), log=log)
+        rec["config_report"] = config_report(dev, q720=(s["Q"], s["K"], s["V"]), log=log)
     if not args.no_cpu_baseline and not args.dense and not args.uneven:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         s = scales[-1]
