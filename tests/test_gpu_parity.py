@@ -745,6 +745,47 @@ def test_step_captured_in_a_graph_replays_exactly():
         assert torch.equal(out, ref), rep
 
 
+
+def test_queued_attention_captured_in_a_graph_replays_exactly():
+    """The attention on the persistent grid (480p: 732 rows per XCD queue, so the atomic queues are
+    used) and the balanced call, captured in one HIP graph with caller-owned workspaces: the queue
+    counters are set by a kernel inside the graph, so every replay, with eager work on the same
+    buffers in between, equals the eager calls bit for bit."""
+    cfg = I.S480P
+    sc = scale_of(cfg)
+    Q, K, V = inputs(cfg)
+    print_case("graph queues", cfg.name)
+    _, _, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, 0.25)
+    p = S.problem(Q, K, V, sc)
+    qws = torch.zeros((S.bsa_workspace_bytes(p) // 4,), dtype=torch.int32, device=DEV)
+    bws = torch.zeros((S.balance_workspace_bytes(p) // 4,), dtype=torch.int32, device=DEV)
+    ref, ref_lse = S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, return_lse=True, workspace=qws)
+    ref_b = S.sparstar_bsa_fwd_balanced(Q, K, V, rp, ci, sc, workspace=bws)
+    assert torch.equal(ref, ref_b)
+    out, out_b = torch.empty_like(Q), torch.empty_like(Q)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _, lse_graph = S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, out=out, return_lse=True, workspace=qws)
+        S.sparstar_bsa_fwd_balanced(Q, K, V, rp, ci, sc, out=out_b, workspace=bws)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        out_b.fill_(float("nan"))
+        lse_graph.fill_(float("nan"))
+        qws.fill_(-7)   # stale counters: the graph must set them itself
+        bws.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse_graph, ref_lse), rep
+        assert torch.equal(out_b, ref), rep
+        # eager work on the same buffers between replays
+        S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, out=out, workspace=qws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+
+
 # ---------------------------------------------------------------- full size (sampled)
 
 _SCORES = {}

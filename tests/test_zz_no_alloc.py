@@ -48,3 +48,30 @@ def test_noalloc_equals_balanced_on_two_calls(uneven):
         S.sparstar_bsa_fwd_balanced_noalloc(Q, K, V, rp, ci, scale, out, lse)
         torch.cuda.synchronize()
         assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+
+
+def test_noalloc_captured_in_a_graph_replays_exactly():
+    """The callers the allocation-free entry point is for include code under HIP graph capture:
+    captured once (its queues engaged: 256 rows per XCD queue), every replay, with eager calls
+    of it in between, equals the balanced call with its own workspace bit for bit."""
+    print("CASE noalloc graph", flush=True)
+    Q, K, V, scale, rp, ci = _problem(512, 3000, 16384, 16, 128, 31, True)
+    ref, ref_lse = S.sparstar_bsa_fwd_balanced(Q, K, V, rp, ci, scale, return_lse=True)
+    out = torch.empty_like(Q)
+    lse = torch.empty(Q.shape[:3], dtype=torch.float32, device=DEV)
+    S.sparstar_bsa_fwd_balanced_noalloc(Q, K, V, rp, ci, scale, out, lse)  # first call on the device: eager
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.sparstar_bsa_fwd_balanced_noalloc(Q, K, V, rp, ci, scale, out, lse)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse), rep
+        out.fill_(float("nan"))
+        S.sparstar_bsa_fwd_balanced_noalloc(Q, K, V, rp, ci, scale, out, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
