@@ -18,6 +18,9 @@ inputs already resident in HBM.  Prints one JSON line:
   sustained    steps run back to back for --sustain seconds with the board
                power and the XCD clocks sampled through amd-smi, and the bf16
                MFMA peak at the sampled clock
+  mfma_probe   the bf16 MFMA rate the part sustains on random operands (a probe
+               kernel of the library), whose rate roofline reports beside the
+               published peak as achievable_peak / frac_of_achievable
 
 --dense times dense_attn_fwd instead (the density-1 baseline); --mass measures
 the retained attention mass of the selection strategies and times the
@@ -87,6 +90,9 @@ def parse():
     ap.add_argument("--sustain", type=float, default=5.0,
                     help="seconds of back-to-back steps after the timed ones, with the board power and the "
                          "XCD clocks sampled through amd-smi (0: skip)")
+    ap.add_argument("--mfma-probe", type=float, default=3.0,
+                    help="seconds of the matrix-core rate probe on random operands after the steps, with "
+                         "amd-smi sampled: the achievable bf16 MFMA peak (0: skip)")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -377,10 +383,10 @@ def _smi_sample():
         return None
 
 
-def sustained_run(step, seconds, flops, achieved_short):
-    """Steps back to back for `seconds`, with amd-smi sampled from a second thread.  Reports the
-    sustained time per step, the board power and the XCD clocks, and the bf16 MFMA peak at the
-    sampled clock (the published peak is quoted at 2.4 GHz)."""
+def _run_sampled(fn, seconds):
+    """Calls fn() (which enqueues GPU work) back to back for `seconds`, synchronising every four
+    calls, with amd-smi sampled from a second thread.  Returns (calls, wall seconds, GPU ms from
+    HIP events around all calls, the readings after the first second: the clocks ramp up from idle)."""
     import threading
     import torch
     samples, stop = [], threading.Event()
@@ -392,34 +398,72 @@ def sustained_run(step, seconds, flops, achieved_short):
                 samples.append(r)
             stop.wait(0.25)
 
-    step()
+    fn()
     torch.cuda.synchronize()
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n, t0 = 0, time.perf_counter()
+    e0.record()
     while time.perf_counter() - t0 < seconds:
         for _ in range(4):
-            step()
+            fn()
         torch.cuda.synchronize()
         n += 4
+    e1.record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stop.set()
     th.join(timeout=15)
+    busy = samples[len(samples) // max(1, int(seconds)):] if samples else []
+    return n, wall, e0.elapsed_time(e1), samples, busy
+
+
+def _smi_summary(busy):
+    pw = [x["power_w"] for x in busy]
+    clk = [float(np.mean(x["gfx_mhz"])) for x in busy]
+    return {"socket_power_w": {"mean": float(np.mean(pw)), "max": float(max(pw))},
+            "xcd_clock_mhz": {"mean": float(np.mean(clk)), "min": min(min(x["gfx_mhz"]) for x in busy),
+                              "max": max(max(x["gfx_mhz"]) for x in busy)},
+            "mem_clock_mhz": busy[-1]["mem_mhz"]}
+
+
+def sustained_run(step, seconds, flops, achieved_short):
+    """Steps back to back for `seconds`, with amd-smi sampled from a second thread.  Reports the
+    sustained time per step, the board power and the XCD clocks, and the bf16 MFMA peak at the
+    sampled clock (the published peak is quoted at 2.4 GHz)."""
+    n, wall, _, samples, busy = _run_sampled(step, seconds)
     rec = {"seconds": wall, "steps": n, "ms_per_step": wall * 1e3 / n, "tflops": flops * n / wall / 1e12,
            "smi_samples": len(samples), "source": "amd-smi metric -p -c --json"}
-    # Drop the readings of the first second (the clocks ramp up from idle).
-    busy = samples[len(samples) // max(1, int(seconds)):] if samples else []
     if busy:
-        pw = [x["power_w"] for x in busy]
-        clk = [float(np.mean(x["gfx_mhz"])) for x in busy]
-        lo = min(min(x["gfx_mhz"]) for x in busy)
-        hi = max(max(x["gfx_mhz"]) for x in busy)
-        mhz = float(np.mean(clk))
-        rec.update({"socket_power_w": {"mean": float(np.mean(pw)), "max": float(max(pw))},
-                    "xcd_clock_mhz": {"mean": mhz, "min": lo, "max": hi},
-                    "mem_clock_mhz": busy[-1]["mem_mhz"],
-                    "bf16_peak_at_clock_tflops": PEAK_BF16_TFLOPS * mhz / 2400.0,
+        rec.update(_smi_summary(busy))
+        mhz = rec["xcd_clock_mhz"]["mean"]
+        rec.update({"bf16_peak_at_clock_tflops": PEAK_BF16_TFLOPS * mhz / 2400.0,
                     "attention_frac_at_clock": achieved_short / (PEAK_BF16_TFLOPS * mhz / 2400.0)})
+    return rec
+
+
+def mfma_probe_run(dev, seconds, rounds=2000):
+    """The bf16 matrix-core rate the part sustains on random operands (sparstar_mfma_probe: the
+    attention's MFMA instruction, eight chains per wavefront, two wavefronts per SIMD, a new
+    operand pair for every instruction), launched back to back for `seconds` with amd-smi
+    sampled: the achievable peak against which the attention's rate can be read."""
+    import torch
+    from block_sparse_attention_aggregated_amd import sparstar as S
+    sink = torch.empty((max(S.mfma_probe_sink_len(), 1),), dtype=torch.float32, device=dev)
+    per_launch = []
+
+    def launch():
+        per_launch.append(S.sparstar_mfma_probe(rounds, sink))
+
+    n, wall, gpu_ms, samples, busy = _run_sampled(launch, seconds)
+    flops = per_launch[-1] * n
+    rec = {"tflops": flops / (gpu_ms * 1e-3) / 1e12, "launches": n, "seconds": wall,
+           "ms_per_launch": gpu_ms / n, "rounds": rounds,
+           "operands": "bf16 uniform in [-2, 2) from a counter hash, a new pair for every instruction",
+           "smi_samples": len(samples), "source": "amd-smi metric -p -c --json"}
+    if busy:
+        rec.update(_smi_summary(busy))
     return rec
 
 
@@ -733,6 +777,12 @@ def main():
         print(f"# {args.sustain:.0f} s of back-to-back steps with power and clock sampling", file=sys.stderr,
               flush=True)
         rec["sustained"] = sustained_run(step, args.sustain, flops, achieved)
+    if args.mfma_probe > 0:
+        print(f"# {args.mfma_probe:.0f} s of the matrix-core rate probe", file=sys.stderr, flush=True)
+        probe = mfma_probe_run(dev, args.mfma_probe)
+        rec["mfma_probe"] = probe
+        rec["roofline"]["achievable_peak"] = probe["tflops"]
+        rec["roofline"]["frac_of_achievable"] = achieved / probe["tflops"]
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

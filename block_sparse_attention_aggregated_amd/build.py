@@ -23,7 +23,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparstar.so")
 
 SOURCES = ["host.cpp", "pool_score.hip", "select.hip", "score_select.hip", "attn_mfma.hip", "attn_simt.hip", "mass.hip",
-           "balance.hip"]
+           "balance.hip", "mfma_probe.hip"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -668,4 +668,29 @@ sparstar_status sparstar_bsa_fwd_balanced_noalloc(const sparstar_problem* p, con
   });
 }
 
+int64_t sparstar_mfma_probe_sink_len(void) {
+  const int64_t wgs = sparstar::mfma_probe_workgroups();
+  return wgs > 0 ? wgs * 256 : -1;
+}
+
+sparstar_status sparstar_mfma_probe(int32_t rounds, float* sink, int64_t sink_len, double* flops, void* stream) {
+  return guarded([&]() -> sparstar_status {
+    if (rounds < 1) return fail(SPARSTAR_ERR_SHAPE, "rounds must be >= 1, got %d", rounds);
+    if (!sink) return fail(SPARSTAR_ERR_NULL, "sink must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(sink) & 3u) return fail(SPARSTAR_ERR_LAYOUT, "sink must be 4-byte aligned");
+    sparstar_status s = check_device();
+    if (s != SPARSTAR_OK) return s;
+    const int64_t wgs = sparstar::mfma_probe_workgroups();
+    if (wgs <= 0) return fail(SPARSTAR_ERR_HIP, "could not query the CU count");
+    if (sink_len < wgs * 256)
+      return fail(SPARSTAR_ERR_CAPACITY, "sink of %lld floats, %lld needed", (long long)sink_len,
+                  (long long)(wgs * 256));
+    if ((s = launched(sparstar::launch_mfma_probe(rounds, sink, wgs, (hipStream_t)stream), "mfma_probe launch")) !=
+        SPARSTAR_OK)
+      return s;
+    if (flops) *flops = sparstar::mfma_probe_flops(rounds, wgs);
+    return ok();
+  });
+}
+
 }  // extern "C"

@@ -121,6 +121,12 @@ hipError_t launch_row_ptr(int32_t* row_ptr, int64_t rows, int32_t per_row, hipSt
 // Largest n_k the fused score-and-select kernel holds (a strip's keys in LDS).
 int score_select_max_keys();
 hipError_t launch_score_select(const ScoreSelectArgs& a, hipStream_t s);
+
+// Matrix-core rate probe (measurement helper): workgroups per launch on the current
+// device (-1 on error), the launch, and the multiply-add flops of one launch.
+int64_t mfma_probe_workgroups();
+hipError_t launch_mfma_probe(int32_t rounds, float* sink, int64_t workgroups, hipStream_t s);
+double mfma_probe_flops(int32_t rounds, int64_t workgroups);
 // Attention row mapping: the query blocks of a head are split into S contiguous
 // segments of per = ceil(n_q / S) blocks; workgroup id w runs on XCD
 // x = w % kXcds, which takes segment x % S of head (w / kXcds / per) * (kXcds / S)

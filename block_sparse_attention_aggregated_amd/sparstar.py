@@ -71,6 +71,8 @@ _SIGS = {
                                 _c_vp]),
     "sparstar_balance_workspace_bytes": (_c_i64, [ctypes.POINTER(Problem)]),
     "sparstar_attention_kernel": (_c_i32, [ctypes.POINTER(Problem)]),
+    "sparstar_mfma_probe_sink_len": (_c_i64, []),
+    "sparstar_mfma_probe": (_c_i32, [_c_i32, _c_vp, _c_i64, ctypes.POINTER(ctypes.c_double), _c_vp]),
     "sparstar_bsa_fwd_balanced": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
                                            _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "sparstar_bsa_fwd_balanced_noalloc": (_c_i32, [ctypes.POINTER(Problem), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
@@ -199,6 +201,22 @@ def balance_workspace_bytes(p: Problem) -> int:
 def attention_kernel(p: Problem) -> int:
     """KERNEL_MFMA_BF16 or KERNEL_F32: which attention kernel the problem runs on (-1 if invalid)."""
     return lib().sparstar_attention_kernel(ctypes.byref(p))
+
+
+def mfma_probe_sink_len() -> int:
+    """Floats the sink of sparstar_mfma_probe needs on the current device (-1 if unknown)."""
+    return lib().sparstar_mfma_probe_sink_len()
+
+
+def sparstar_mfma_probe(rounds: int, sink: torch.Tensor) -> float:
+    """One launch of the matrix-core rate probe on the current stream (a measurement helper,
+    not a step of the method); returns the launch's multiply-add flops."""
+    if sink.dtype != torch.float32 or not sink.is_contiguous():
+        raise SparstarError(ERR_SHAPE, "sink must be contiguous float32")
+    flops = ctypes.c_double(0.0)
+    _check(lib().sparstar_mfma_probe(int(rounds), _ptr(sink), sink.numel(), ctypes.byref(flops),
+                                     _stream(sink.device)))
+    return flops.value
 
 
 def status_string(s: int) -> str:

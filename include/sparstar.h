@@ -318,6 +318,27 @@ sparstar_status sparstar_token_topk_mass(const sparstar_problem* p, const void* 
                                          int64_t keep_tokens, int64_t k_tokens, float* out,
                                          void* stream);
 
+/* ---------------- measurement helper (not a step of the method) --------------------------
+ * The bf16 matrix-core rate the GPU sustains on operands like the attention's, against
+ * which the attention's own rate can be read (its published peak assumes a clock the
+ * part does not hold under this load).  Each lane of two 4-wavefront workgroups per CU
+ * runs eight independent chains of v_mfma_f32_32x32x16_bf16 (the attention's
+ * instruction) on operands drawn from a counter hash, uniform in [-2, 2), a new operand
+ * pair for every instruction; fixed operands would draw less power and overstate it. */
+
+/* Floats the sink of sparstar_mfma_probe must hold on the current device (256 per
+ * workgroup, two workgroups per CU); -1 if the device cannot be queried. */
+int64_t sparstar_mfma_probe_sink_len(void);
+
+/* One launch of `rounds` rounds (64 instructions per wavefront each) on `stream`.
+ *   sink : out, device float32 [sink_len], one value per lane (keeps the chains live).
+ *   flops: out, host, nullable: the multiply-add flops of the launch (2*32*32*16 per
+ *          instruction); divide by the launch time for the rate.
+ * SPARSTAR_ERR_SHAPE if rounds < 1, SPARSTAR_ERR_NULL for a NULL sink,
+ * SPARSTAR_ERR_LAYOUT if it is not 4-byte aligned, SPARSTAR_ERR_CAPACITY if sink_len
+ * is below sparstar_mfma_probe_sink_len(). */
+sparstar_status sparstar_mfma_probe(int32_t rounds, float* sink, int64_t sink_len, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

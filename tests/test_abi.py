@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 24
+    assert "sparstar_bsa_fwd" in names and "dense_attn_fwd" in names and len(names) == 26
+    assert {"sparstar_mfma_probe", "sparstar_mfma_probe_sink_len"} <= set(names)
     assert {"sparstar_pool_blocks", "sparstar_score_select"} <= set(names)
     assert {"sparstar_block_mass", "sparstar_selection_mass", "sparstar_window_scores",
             "sparstar_token_topk_mass"} <= set(names)
@@ -275,3 +276,14 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(S, "LIB_PATH", "/nonexistent/libsparstar.so")
     with pytest.raises(S.SparstarError):
         S.lib()
+
+
+def test_mfma_probe_validates_before_any_device_call():
+    L = S.lib()
+    flops = ctypes.c_double(-1.0)
+    b = ctypes.c_void_p(BOGUS)
+    assert L.sparstar_mfma_probe(0, b, 1 << 20, ctypes.byref(flops), None) == S.ERR_SHAPE
+    assert L.sparstar_mfma_probe(-5, b, 1 << 20, ctypes.byref(flops), None) == S.ERR_SHAPE
+    assert L.sparstar_mfma_probe(10, None, 1 << 20, ctypes.byref(flops), None) == S.ERR_NULL
+    assert L.sparstar_mfma_probe(10, ctypes.c_void_p(BOGUS + 2), 1 << 20, ctypes.byref(flops), None) == S.ERR_LAYOUT
+    assert flops.value == -1.0   # nothing written on an error

@@ -23,7 +23,7 @@ def test_help_lists_the_modes():
     r = _run("--help")
     assert r.returncode == 0
     for opt in ("--workload", "--density", "--dense", "--mass", "--uneven", "--balanced", "--fused-select", "--no-cpu-baseline",
-                "--steps", "--warmup", "--sustain", "--no-report"):
+                "--steps", "--warmup", "--sustain", "--no-report", "--mfma-probe"):
         assert opt in r.stdout, opt
 
 

@@ -786,6 +786,21 @@ def test_queued_attention_captured_in_a_graph_replays_exactly():
         assert torch.equal(out, ref), rep
 
 
+
+def test_mfma_probe_runs_and_counts_its_flops():
+    """The matrix-core rate probe (a measurement helper): its sink size follows the CU count, a
+    launch fills every lane's value with a finite number, and its flop count is the formula's."""
+    n = S.mfma_probe_sink_len()
+    props = torch.cuda.get_device_properties(0)
+    assert n == 2 * props.multi_processor_count * 256
+    sink = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+    flops = S.sparstar_mfma_probe(4, sink)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()
+    assert flops == 2 * props.multi_processor_count * 4 * 4 * 64 * (2 * 32 * 32 * 16)
+    with pytest.raises(S.SparstarError):
+        S.sparstar_mfma_probe(4, sink[: n - 1])
+
 # ---------------------------------------------------------------- full size (sampled)
 
 _SCORES = {}
