@@ -8,8 +8,8 @@
 // Shape: bf16 Q/K/V, head_dim 128, query and key blocks of b = 64, 128 or 256
 // tokens.  One workgroup of b / 32 wavefronts per query block (two workgroups
 // per CU for b <= 128, one for b = 256); wavefront w owns queries 32w .. 32w+31
-// of the block.  Each key block is processed as b / 64 sub-tiles of 64 keys,
-// double-buffered in LDS.  Per sub-tile:
+// of the block.  Each key block is processed as sub-tiles of 64 keys (32 at
+// b = 64), double-buffered in LDS.  Per 64-key sub-tile:
 //   S^T[key, query] = K Q^T   16 x v_mfma_f32_32x32x16_bf16 per wavefront in
 //                             two independent accumulator chains (A = K from
 //                             LDS, B = Q held in registers for the whole row),
@@ -45,8 +45,9 @@
 // conflicts without padding.  One barrier per sub-tile.  The block lists are
 // read through the scalar cache.
 //
-// XCD-aware row queues, run by a persistent grid.  Rows are queued per XCD.  A head's query blocks are split into S contiguous segments of
-// per = ceil(n_q / S) blocks; the queue of XCD x holds segment x % S of head
+// XCD-aware row queues, run by a persistent grid.  Rows are queued per XCD: a
+// head's query blocks are split into S contiguous segments of per = ceil(n_q / S)
+// blocks; the queue of XCD x holds segment x % S of head
 // (8 / S) j + x / S for j = 0, 1, ... in order, so the rows resident on one XCD
 // are consecutive query blocks of one head, whose overlapping block lists share
 // that XCD's L2, and the GPU works on 8 / S heads at a time, whose K and V stay
@@ -69,6 +70,8 @@
 //              persistent grid with a fixed share of rows per workgroup measured
 //              slower than both: its workgroups drift apart, and the rows in
 //              flight on an XCD stop being neighbours.)
+// The dynamic queues run when the caller passes their counters and each XCD has
+// at least two rounds of rows; otherwise the static ones.
 // With a row order (uneven lists), each segment's rows run longest list first.
 
 #include "sparstar_internal.h"

@@ -1,6 +1,7 @@
 // Float32 path: block-sparse (and dense) attention forward for float32
-// inputs and for the shapes the MFMA kernel does not cover (head_dim 64).  Same semantics as the MFMA kernel ("SparSTAR: Sparse
-// Attention for SpaceTime AutoRegressive Video Synthesis", section 5
+// inputs and for the shapes the MFMA kernel does not cover (head_dim 64).  Same
+// semantics as the MFMA kernel ("SparSTAR: Sparse Attention for SpaceTime
+// AutoRegressive Video Synthesis", section 5
 // "Forward-Only Sparse Execution"): every query of block i attends, with a
 // softmax over real keys only, to the key blocks listed for row i.
 //
