@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ms/scale and effective TFLOP/s (executed blocks) at 72k-token 720p scale"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X float32 vector, published (the float32 attention kernel's bound)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsa_fwd_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_aggregated_amd", "csrc", "attn_mfma.hip")
 
@@ -557,13 +558,18 @@ def scale_report(cfg, density, dev, reps=5, warmup=2, dense=False, inputs=None, 
                    scoring_hbm_frac=scoring_bytes(cfg) / (t_pool * 1e-3) / 1e9 / PEAK_HBM_GBS)
     rec["exec_tflop"] = flops / 1e12
     rec["attention_tflops"] = flops / (t_att * 1e-3) / 1e12
-    rec["attention_bf16_peak_frac"] = rec["attention_tflops"] / PEAK_BF16_TFLOPS
+    if cfg.dtype == "bf16":
+        rec["attention_bf16_peak_frac"] = rec["attention_tflops"] / PEAK_BF16_TFLOPS
+    else:  # the float32 kernel: vector FMAs, not the matrix cores
+        rec["attention_bf16_peak_frac"] = None
+        rec["attention_f32_peak_frac"] = rec["attention_tflops"] / PEAK_FP32_TFLOPS
     rec["step_tflops"] = flops / (rec["ms_scale"] * 1e-3) / 1e12
     return rec
 
 
 def config_report(dev, q720=None, log=lambda m: None):
-    """ms per scale, effective TFLOP/s and the fraction of the bf16 MFMA peak on every configuration:
+    """ms per scale, effective TFLOP/s and the fraction of the peak on every configuration: the tiny
+    float32 workload (0.5 and 1.0, against the float32 vector peak: it runs the float32 kernel),
     192p (0.3), 480p (0.25), 720p at 0.1, 0.2, 0.4 and 1.0 (dense), the four-scale 720p sweep (0.2
     each), and dense over sparse at 720p, density 0.1 (the analog of the pages' operator speed-up)."""
     import torch
@@ -571,6 +577,14 @@ def config_report(dev, q720=None, log=lambda m: None):
     from block_sparse_attention_aggregated_amd import inputs as I
     flush = infinity_cache_flush(dev)
     rows = []
+    log("report: tiny")
+    tiny = I.make_inputs(I.TINY, device=dev)
+    rows.append(scale_report(I.TINY, 0.5, dev, inputs=tiny, flush=flush))
+    rows.append(scale_report(I.TINY, 1.0, dev, reps=5, warmup=2, dense=True, inputs=tiny))
+    for r in rows:
+        r["note"] = ("a parity workload: 256 queries in 8 workgroups of the float32 kernel (one thread per "
+                     "query) leave the GPU idle, so its time is launch and latency, not throughput")
+    del tiny
     for cfg in (I.S192P, I.S480P):
         log(f"report: {cfg.name}")
         rows.append(scale_report(cfg, cfg.densities[0], dev, flush=flush))
@@ -590,7 +604,7 @@ def config_report(dev, q720=None, log=lambda m: None):
         torch.cuda.empty_cache()
     rows += sweep
     r01 = next(r for r in rows if r["workload"] == "720p" and r["density"] == 0.1)
-    dense = next(r for r in rows if r.get("mode") == "dense")
+    dense = next(r for r in rows if r.get("mode") == "dense" and r["workload"] == "720p")
     flops = sum(r["exec_tflop"] for r in sweep)
     ms = sum(r["ms_scale"] for r in sweep)
     return {
