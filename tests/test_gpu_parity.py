@@ -801,6 +801,26 @@ def test_mfma_probe_runs_and_counts_its_flops():
     with pytest.raises(S.SparstarError):
         S.sparstar_mfma_probe(4, sink[: n - 1])
 
+
+def test_persistent_queues_repeat_bitwise():
+    """Launch after launch on the persistent grid (480p: 732 rows per XCD queue, rows handed out in
+    finishing order): 100 launches reusing one workspace, each output equal to the first bit for
+    bit, since every row is computed whole by one workgroup whichever workgroup pops it."""
+    cfg = I.S480P
+    sc = scale_of(cfg)
+    Q, K, V = inputs(cfg)
+    print_case("repeat queues", cfg.name)
+    _, _, scores = S.sparstar_pool_score(Q, K, sc)
+    rp, ci = S.sparstar_select_blocks(scores, Q, K, sc, 0.25)
+    ws = torch.zeros((S.bsa_workspace_bytes(S.problem(Q, K, V, sc)) // 4,), dtype=torch.int32, device=DEV)
+    ref = S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, workspace=ws)
+    out = torch.empty_like(ref)
+    bad = 0
+    for _ in range(100):
+        S.sparstar_bsa_fwd(Q, K, V, rp, ci, sc, out=out, workspace=ws)
+        bad += int(not torch.equal(out, ref))
+    assert bad == 0
+
 # ---------------------------------------------------------------- full size (sampled)
 
 _SCORES = {}
